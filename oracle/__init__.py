@@ -1,0 +1,332 @@
+"""Float64 CPU oracle for Windowed-MTP draft attention, full draft attention, verification
+attention and the compact ring buffer.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package; the product path (``draft_attention_amd``) never does, and
+this package never imports the product path. The two share no code.
+
+Everything here restates the Windowed-MTP abstract (thelatestinai.com/papers/2607.21535; the same
+text appears on the khansong-paper-with-me page) in plain code:
+
+* the native MTP draft head attends over the entire KV cache at every draft step (abstract,
+  third sentence) -- :func:`full_positions`;
+* Windowed-MTP gives the draft's attention a StreamingLLM-style sliding window plus attention
+  sinks, and leaves full-attention verification intact (abstract, fifth sentence) --
+  :func:`windowed_positions`, :func:`verify_positions`;
+* the draft KV that is never read is reclaimed by a compact ring buffer (abstract, last sentence)
+  -- :func:`ring_slot`, :class:`RingModel`.
+
+The pages give no formula, no layout and no values for S, W or the slot map. The readings taken
+here (listed with reasons in the design notes of the repository):
+
+* sinks are the first S positions of the sequence, 0..S-1;
+* each draft step appends its own K/V before attending, so the window is the last W of the n
+  cached positions and includes the current token;
+* sink and window sets are united with each position taken once (so S + W >= n gives full
+  attention);
+* GQA: query head hq reads KV head hq // G with G = Hq / Hkv;
+* ring slot of position p: p for p < S, else S + (p - S) mod W (the first window token lands in
+  slot S); a contiguous cache is the same map with S = capacity, W = 0;
+* verification query j of m (the candidates sit at positions n-m .. n-1) attends positions
+  0 .. n-m+j, its own included;
+* outputs and lse are float64 here; lse uses the natural log; an empty set gives o = 0 and
+  lse = -inf.
+
+The arithmetic of each attention problem is in ``wmtp_oracle.c`` (two-pass softmax in float64);
+this module decides which rows each problem attends.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "wmtp_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16, F64 = 0, 1, 2
+
+Range = Tuple[int, int]  # half-open [start, stop)
+
+
+# --------------------------------------------------------------------------------------------
+# build / load of the C core
+# --------------------------------------------------------------------------------------------
+def build(verbose: bool = False) -> str:
+    """Compile ``wmtp_oracle.c`` into ``liboracle.so`` with gcc (plain -O2, OpenMP, IEEE)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("q_off", ctypes.c_int64), ("kv_off", ctypes.c_int64 * 2),
+                ("count", ctypes.c_int64 * 2), ("row_stride", ctypes.c_int64),
+                ("out_off", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.wmtp_oracle_attention.restype = ctypes.c_int
+        lib.wmtp_oracle_attention.argtypes = [
+            ctypes.c_int64, ctypes.POINTER(_Problem), ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+        lib.wmtp_oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().wmtp_oracle_max_threads())
+
+
+# --------------------------------------------------------------------------------------------
+# which positions each problem attends
+# --------------------------------------------------------------------------------------------
+def full_positions(n: int) -> List[Range]:
+    """Native draft head: every cached position 0..n-1 (abstract, third sentence)."""
+    return [(0, max(0, n))]
+
+
+def windowed_positions(n: int, S: int, W: int) -> List[Range]:
+    """Windowed-MTP draft head: attention sinks {p < S} united with the sliding window of the
+    last W cached positions {n-W <= p < n} (abstract, fifth sentence), each position once."""
+    if W < 1 or S < 0:
+        raise ValueError("windowed attention needs W >= 1 and S >= 0")
+    n = max(0, n)
+    sink_stop = min(S, n)
+    win_start = max(sink_stop, n - W)
+    return [(0, sink_stop), (win_start, n)]
+
+
+def verify_positions(n: int, m: int, j: int) -> List[Range]:
+    """Full-attention verification (abstract, fifth sentence): the m candidates occupy positions
+    n-m .. n-1 and candidate j sees the whole prefix plus candidates 0..j."""
+    return [(0, max(0, n - m + j + 1))]
+
+
+def dropped_fraction(n: int, S: int, W: int) -> float:
+    """Share of the n cached draft KV entries that the windowed draft never reads."""
+    kept = sum(b - a for a, b in windowed_positions(n, S, W))
+    return 1.0 - kept / n
+
+
+# --------------------------------------------------------------------------------------------
+# the compact ring buffer (abstract, last sentence)
+# --------------------------------------------------------------------------------------------
+def ring_slot(p, S: int, W: int):
+    """Slot of logical position p: sinks are pinned, window positions wrap over W slots.
+    Works on Python ints and numpy integer arrays."""
+    if W == 0:
+        return p
+    if isinstance(p, np.ndarray):
+        return np.where(p < S, p, S + (p - S) % W)
+    return p if p < S else S + (p - S) % W
+
+
+class RingModel:
+    """Host simulation of every append into per-sequence ring buffers of S + W slots.
+
+    ``tags[b, s]`` is the logical position held in slot s of sequence b (-1: never written),
+    ``n[b]`` the number of tokens appended so far. Appends are applied token by token in
+    position order, so a later token always overwrites an earlier one in the same slot.
+    """
+
+    def __init__(self, batch: int, S: int, W: int):
+        self.S, self.W = S, W
+        self.tags = np.full((batch, S + W), -1, dtype=np.int64)
+        self.n = np.zeros(batch, dtype=np.int64)
+
+    def append(self, b: int, count: int) -> None:
+        if count <= 0:
+            return
+        p = np.arange(self.n[b], self.n[b] + count, dtype=np.int64)
+        s = ring_slot(p, self.S, self.W)
+        # positions increase, so "last writer wins" is the per-slot maximum
+        np.maximum.at(self.tags[b], s, p)
+        self.n[b] += count
+
+    def occupied_slots(self, b: int) -> np.ndarray:
+        return np.nonzero(self.tags[b] >= 0)[0]
+
+
+# --------------------------------------------------------------------------------------------
+# KV rows addressed by logical position
+# --------------------------------------------------------------------------------------------
+@dataclass
+class LogicalKV:
+    """K and V rows of B sequences, ``[B][Hkv][R][d]``, together with the logical positions they
+    hold. ``segments[b]`` lists ``(first_position, first_row, count)`` runs; a full contiguous
+    sequence is the single run ``(0, 0, R)``. ``k`` and ``v`` are float32, float64 or uint16
+    (bf16 bit patterns, ``dtype=BF16``)."""
+
+    k: np.ndarray
+    v: np.ndarray
+    dtype: int
+    segments: Sequence[Sequence[Tuple[int, int, int]]]
+
+    @property
+    def shape(self):
+        return self.k.shape
+
+    def row_run(self, b: int, p0: int, p1: int) -> Tuple[int, int]:
+        """(first_row, count) of the rows holding positions [p0, p1); they must be one run."""
+        if p1 <= p0:
+            return 0, 0
+        for first_pos, first_row, count in self.segments[b]:
+            if first_pos <= p0 and p1 <= first_pos + count:
+                return first_row + (p0 - first_pos), p1 - p0
+        raise KeyError(f"positions [{p0},{p1}) of sequence {b} are not held as one run")
+
+    def rows_of_positions(self, b: int, h: int, positions: np.ndarray, which: str = "k"):
+        arr = self.k if which == "k" else self.v
+        out = np.empty((len(positions), arr.shape[-1]), dtype=arr.dtype)
+        for i, p in enumerate(positions):
+            r, _ = self.row_run(b, int(p), int(p) + 1)
+            out[i] = arr[b, h, r]
+        return out
+
+
+def contiguous_kv(k: np.ndarray, v: np.ndarray, dtype: int) -> LogicalKV:
+    """K/V ``[B][Hkv][n][d]`` holding positions 0..n-1 of every sequence."""
+    B, _, n, _ = k.shape
+    return LogicalKV(k, v, dtype, [[(0, 0, n)] for _ in range(B)])
+
+
+def _np_dtype_code(a: np.ndarray, declared: int) -> int:
+    if declared == BF16:
+        assert a.dtype == np.uint16, "bf16 arrays are passed as uint16 bit patterns"
+        return BF16
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"unsupported array dtype {a.dtype}")
+
+
+# --------------------------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------------------------
+def attention(q: np.ndarray, q_dtype: int, kv: LogicalKV, sets, scale: float,
+              nthreads: int = 0):
+    """Softmax attention of every query row over its own set of positions.
+
+    ``q`` is ``[B][m][Hq][d]``; ``sets[b][j]`` is the list of position ranges that query token j
+    of sequence b attends (shared by its Hq heads); query head hq reads KV head hq // G.
+    Returns ``(out [B][m][Hq][d] float64, lse [B][m][Hq] float64)``.
+    """
+    q = np.ascontiguousarray(q)
+    B, m, Hq, d = q.shape
+    kb, Hkv, R, dk = kv.k.shape
+    assert kb == B and dk == d and Hq % Hkv == 0
+    G = Hq // Hkv
+    k = np.ascontiguousarray(kv.k)
+    v = np.ascontiguousarray(kv.v)
+    qcode = _np_dtype_code(q, q_dtype)
+    kvcode = _np_dtype_code(k, kv.dtype)
+    probs = (_Problem * (B * m * Hq))()
+    i = 0
+    for b in range(B):
+        for j in range(m):
+            ranges = [r for r in sets[b][j] if r[1] > r[0]]
+            if len(ranges) > 2:
+                raise ValueError("at most two position ranges per problem")
+            for hq in range(Hq):
+                h = hq // G
+                pr = probs[i]
+                pr.q_off = ((b * m + j) * Hq + hq) * d
+                pr.row_stride = d
+                pr.out_off = ((b * m + j) * Hq + hq) * d
+                for run in range(2):
+                    if run < len(ranges):
+                        r0, cnt = kv.row_run(b, ranges[run][0], ranges[run][1])
+                        pr.kv_off[run] = ((b * Hkv + h) * R + r0) * d
+                        pr.count[run] = cnt
+                    else:
+                        pr.kv_off[run] = 0
+                        pr.count[run] = 0
+                i += 1
+    out = np.zeros((B, m, Hq, d), dtype=np.float64)
+    lse = np.zeros((B, m, Hq), dtype=np.float64)
+    rc = _load().wmtp_oracle_attention(
+        len(probs), probs, d, qcode, kvcode, q.ctypes.data, k.ctypes.data, v.ctypes.data,
+        float(scale), out.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    return out, lse
+
+
+def draft_full(q, q_dtype, kv: LogicalKV, n: Sequence[int], scale: float, nthreads: int = 0):
+    """Native draft step: one query token per sequence attends positions 0..n_b-1.
+    ``q`` is ``[B][1][Hq][d]``."""
+    sets = [[full_positions(int(n[b]))] for b in range(q.shape[0])]
+    return attention(q, q_dtype, kv, sets, scale, nthreads)
+
+
+def draft_windowed(q, q_dtype, kv: LogicalKV, n: Sequence[int], S: int, W: int, scale: float,
+                   nthreads: int = 0):
+    """Windowed-MTP draft step over the logical sequence: sinks plus the last W positions."""
+    sets = [[windowed_positions(int(n[b]), S, W)] for b in range(q.shape[0])]
+    return attention(q, q_dtype, kv, sets, scale, nthreads)
+
+
+def verify(q, q_dtype, kv: LogicalKV, n: Sequence[int], scale: float, nthreads: int = 0):
+    """Verification of m candidates (the last m of the n cached positions), causal among them.
+    ``q`` is ``[B][m][Hq][d]``."""
+    m = q.shape[1]
+    sets = [[verify_positions(int(n[b]), m, j) for j in range(m)] for b in range(q.shape[0])]
+    return attention(q, q_dtype, kv, sets, scale, nthreads)
+
+
+def ring_attention(q, q_dtype, ring_k, ring_v, kv_dtype: int, tags: np.ndarray, scale: float,
+                   nthreads: int = 0):
+    """Attention over the occupied slots of ring buffers ``[B][Hkv][S+W][d]`` as the hardware
+    layout holds them (slots in slot order, whatever positions they carry). ``tags[b, s] >= 0``
+    marks an occupied slot."""
+    B = q.shape[0]
+    nslots = ring_k.shape[2]
+    kv = LogicalKV(ring_k, ring_v, kv_dtype, [[(0, 0, nslots)] for _ in range(B)])
+    sets = []
+    for b in range(B):
+        occ = np.nonzero(tags[b] >= 0)[0]
+        runs: List[Range] = []
+        for s in occ:
+            if runs and runs[-1][1] == s:
+                runs[-1] = (runs[-1][0], s + 1)
+            else:
+                runs.append((int(s), int(s) + 1))
+        sets.append([runs])
+    return attention(q, q_dtype, kv, sets, scale, nthreads)
+
+
+def ring_expected(model: RingModel, kv: LogicalKV):
+    """Expected ring contents for the positions recorded in ``model.tags``: K and V arrays
+    ``[B][Hkv][S+W][d]`` (rows of empty slots are zero) gathered from the logical sequence."""
+    B, Hkv, _, d = kv.k.shape
+    nslots = model.tags.shape[1]
+    rk = np.zeros((B, Hkv, nslots, d), dtype=kv.k.dtype)
+    rv = np.zeros((B, Hkv, nslots, d), dtype=kv.v.dtype)
+    for b in range(B):
+        occ = model.occupied_slots(b)
+        pos = model.tags[b, occ]
+        for h in range(Hkv):
+            rk[b, h, occ] = kv.rows_of_positions(b, h, pos, "k")
+            rv[b, h, occ] = kv.rows_of_positions(b, h, pos, "v")
+    return rk, rv

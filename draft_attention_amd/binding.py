@@ -1,0 +1,270 @@
+"""Thin ctypes binding of libwmtp.so (include/wmtp.h). Argument marshalling only: every step of
+the attention and ring paths runs in the HIP kernels behind the C ABI; there is no fallback.
+
+The functions carry the C names. They accept torch tensors (device memory owned by the caller)
+and pass their data pointers, plus the current torch stream unless a stream is given. They return
+the wmtp status code; with ``check=True`` (the default) a nonzero status raises :class:`WmtpError`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwmtp.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "wmtp.h")
+
+WMTP_OK = 0
+WMTP_ERR_INVALID_ARG = 1
+WMTP_ERR_UNSUPPORTED = 2
+WMTP_ERR_CAPACITY = 3
+WMTP_ERR_WORKSPACE = 4
+WMTP_ERR_HIP = 5
+WMTP_F32 = 0
+WMTP_BF16 = 1
+
+
+class WmtpError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class wmtp_kv(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("seq_len", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("sink", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libwmtp.so. Raises if it has not been built: there is no other implementation."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m draft_attention_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        kvp = ctypes.POINTER(wmtp_kv)
+        L.wmtp_ring_append.argtypes = [kvp, vp, vp, i32, vp]
+        L.wmtp_draft_attn_windowed.argtypes = [kvp, vp, i32, f32, vp, vp, vp, sz, vp]
+        L.wmtp_draft_attn_full.argtypes = [kvp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
+        L.wmtp_verify_attn.argtypes = [kvp, vp, i32, i32, f32, i32, vp, vp, vp, sz, vp]
+        L.wmtp_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.wmtp_attn_workspace_bytes.restype = sz
+        L.wmtp_status_string.argtypes = [ctypes.c_int]
+        L.wmtp_status_string.restype = ctypes.c_char_p
+        for name in ("wmtp_ring_append", "wmtp_draft_attn_windowed", "wmtp_draft_attn_full",
+                     "wmtp_verify_attn"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/wmtp.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(wmtp_\w+)\s*\(", text, re.M)))
+
+
+def status_string(status: int) -> str:
+    return lib().wmtp_status_string(int(status)).decode()
+
+
+def _ptr(t) -> Optional[int]:
+    """Device address of a tensor (None stays NULL; ints pass through as raw addresses)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("wmtp: every buffer must be device memory (got a host tensor)")
+    if not t.is_contiguous():
+        raise ValueError("wmtp: buffers must be dense (contiguous) tensors")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _done(status: int, what: str, check: bool) -> int:
+    if check and status != WMTP_OK:
+        raise WmtpError(status, what)
+    return status
+
+
+@dataclass
+class KVCache:
+    """Device tensors of one cache plus its geometry; ``desc()`` gives the C descriptor."""
+
+    k: object
+    v: object
+    pos: object
+    seq_len: object
+    batch: int
+    n_kv_heads: int
+    head_dim: int
+    capacity: int
+    sink: int
+    window: int
+    dtype: int
+
+    @classmethod
+    def allocate(cls, batch, n_kv_heads, head_dim, capacity, sink, window, torch_dtype,
+                 device="cuda", with_pos=True):
+        """Zeroed cache tensors (torch owns the memory). Ring: window >= 1 and
+        capacity = sink + window; contiguous: window = 0 and sink = capacity."""
+        import torch
+
+        shape = (batch, n_kv_heads, capacity, head_dim)
+        k = torch.zeros(shape, dtype=torch_dtype, device=device)
+        v = torch.zeros(shape, dtype=torch_dtype, device=device)
+        pos = (torch.full((batch, capacity), -1, dtype=torch.int32, device=device)
+               if with_pos else None)
+        seq_len = torch.zeros(batch, dtype=torch.int32, device=device)
+        return cls(k, v, pos, seq_len, batch, n_kv_heads, head_dim, capacity, sink, window,
+                   dtype_code(torch_dtype))
+
+    @classmethod
+    def ring(cls, batch, n_kv_heads, head_dim, sink, window, torch_dtype, device="cuda",
+             with_pos=True):
+        return cls.allocate(batch, n_kv_heads, head_dim, sink + window, sink, window,
+                            torch_dtype, device, with_pos)
+
+    @classmethod
+    def contiguous(cls, batch, n_kv_heads, head_dim, capacity, torch_dtype, device="cuda",
+                   with_pos=False):
+        return cls.allocate(batch, n_kv_heads, head_dim, capacity, capacity, 0, torch_dtype,
+                            device, with_pos)
+
+    def desc(self) -> wmtp_kv:
+        return wmtp_kv(_ptr(self.k), _ptr(self.v), _ptr(self.pos), _ptr(self.seq_len),
+                       self.batch, self.n_kv_heads, self.head_dim, self.capacity, self.sink,
+                       self.window, self.dtype)
+
+
+def dtype_code(torch_dtype) -> int:
+    import torch
+
+    if torch_dtype == torch.float32:
+        return WMTP_F32
+    if torch_dtype == torch.bfloat16:
+        return WMTP_BF16
+    raise ValueError(f"unsupported dtype {torch_dtype}")
+
+
+def _desc(cache):
+    return cache.desc() if isinstance(cache, KVCache) else cache
+
+
+def _numel_ok(t, count: int, elem_bytes: int, name: str) -> None:
+    """A tensor handed to the library must hold at least the elements the call reads or writes
+    (the device cannot check this)."""
+    if t is None or isinstance(t, int):
+        return
+    if t.element_size() != elem_bytes:
+        raise ValueError(f"wmtp: {name} has {t.element_size()}-byte elements, expected {elem_bytes}")
+    if t.numel() < count:
+        raise ValueError(f"wmtp: {name} holds {t.numel()} elements, the call needs {count}")
+
+
+def _check_attn(cache, q, m: int, n_q_heads: int, out, lse) -> None:
+    d = _desc(cache)
+    eb = 2 if d.dtype == WMTP_BF16 else 4
+    rows = d.batch * m * n_q_heads
+    _numel_ok(q, rows * d.head_dim, eb, "q")
+    _numel_ok(out, rows * d.head_dim, 4, "out")
+    _numel_ok(lse, rows, 4, "lse")
+
+
+def _check_append(cache, k_new, v_new, n_new: int) -> None:
+    d = _desc(cache)
+    eb = 2 if d.dtype == WMTP_BF16 else 4
+    count = d.batch * max(n_new, 0) * d.n_kv_heads * d.head_dim
+    _numel_ok(k_new, count, eb, "k_new")
+    _numel_ok(v_new, count, eb, "v_new")
+    if isinstance(cache, KVCache):
+        cnt = d.batch * d.n_kv_heads * d.capacity * d.head_dim
+        _numel_ok(cache.k, cnt, eb, "cache.k")
+        _numel_ok(cache.v, cnt, eb, "cache.v")
+        _numel_ok(cache.pos, d.batch * d.capacity, 4, "cache.pos")
+        _numel_ok(cache.seq_len, d.batch, 4, "cache.seq_len")
+
+
+# ------------------------------------------------------------------------------------------
+# the C ABI, one function each
+# ------------------------------------------------------------------------------------------
+def wmtp_ring_append(cache, k_new, v_new, n_new: int, stream=None, check=True) -> int:
+    _check_append(cache, k_new, v_new, n_new)
+    d = _desc(cache)
+    st = lib().wmtp_ring_append(ctypes.byref(d), _ptr(k_new), _ptr(v_new), int(n_new),
+                                _stream(stream))
+    return _done(st, "wmtp_ring_append", check)
+
+
+def wmtp_draft_attn_windowed(ring, q, n_q_heads: int, sm_scale: float, out, lse, ws,
+                             ws_bytes: Optional[int] = None, stream=None, check=True) -> int:
+    _check_attn(ring, q, 1, n_q_heads, out, lse)
+    d = _desc(ring)
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    st = lib().wmtp_draft_attn_windowed(ctypes.byref(d), _ptr(q), int(n_q_heads), float(sm_scale),
+                                        _ptr(out), _ptr(lse), _ptr(ws), int(nbytes),
+                                        _stream(stream))
+    return _done(st, "wmtp_draft_attn_windowed", check)
+
+
+def wmtp_draft_attn_full(cache, q, n_q_heads: int, sm_scale: float, max_seq_len: int, out, lse,
+                         ws, ws_bytes: Optional[int] = None, stream=None, check=True) -> int:
+    _check_attn(cache, q, 1, n_q_heads, out, lse)
+    d = _desc(cache)
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    st = lib().wmtp_draft_attn_full(ctypes.byref(d), _ptr(q), int(n_q_heads), float(sm_scale),
+                                    int(max_seq_len), _ptr(out), _ptr(lse), _ptr(ws), int(nbytes),
+                                    _stream(stream))
+    return _done(st, "wmtp_draft_attn_full", check)
+
+
+def wmtp_verify_attn(cache, q, m: int, n_q_heads: int, sm_scale: float, max_seq_len: int, out,
+                     lse, ws, ws_bytes: Optional[int] = None, stream=None, check=True) -> int:
+    _check_attn(cache, q, m, n_q_heads, out, lse)
+    d = _desc(cache)
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    st = lib().wmtp_verify_attn(ctypes.byref(d), _ptr(q), int(m), int(n_q_heads),
+                                float(sm_scale), int(max_seq_len), _ptr(out), _ptr(lse),
+                                _ptr(ws), int(nbytes), _stream(stream))
+    return _done(st, "wmtp_verify_attn", check)
+
+
+def wmtp_attn_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, m: int,
+                              max_seq_len: int) -> int:
+    return int(lib().wmtp_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, m,
+                                               max_seq_len))
+
+
+def wmtp_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def workspace(batch, n_q_heads, n_kv_heads, head_dim, m, max_seq_len, device="cuda"):
+    """A device byte tensor large enough for an attention call with these sizes."""
+    import torch
+
+    n = wmtp_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, m, max_seq_len)
+    if n == 0:
+        raise ValueError("no attention call accepts these sizes")
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]

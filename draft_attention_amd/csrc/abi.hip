@@ -1,0 +1,170 @@
+// abi.hip -- the extern "C" entry points of libwmtp.so (declared and documented in wmtp.h):
+// host-side validation, split planning and launches. No allocation, no synchronisation, no global
+// state.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "wmtp_internal.h"
+
+namespace {
+
+using wmtp::SplitPlan;
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t plan_bytes(const SplitPlan& p) {
+  return round_up(p.ws_o_floats * sizeof(float), kAlign) + p.ws_ml_floats * sizeof(float);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elem_bytes(int dtype) { return dtype == WMTP_BF16 ? 2 : 4; }
+
+// Checks shared by every call. Returns WMTP_OK or the status to report.
+int check_kv(const wmtp_kv* c) {
+  if (!c) return WMTP_ERR_INVALID_ARG;
+  if (c->dtype != WMTP_F32 && c->dtype != WMTP_BF16) return WMTP_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return WMTP_ERR_UNSUPPORTED;
+  if (!c->k || !c->v || !c->seq_len) return WMTP_ERR_INVALID_ARG;
+  if (c->batch < 1 || c->n_kv_heads < 1 || c->capacity < 1) return WMTP_ERR_INVALID_ARG;
+  if (c->sink < 0 || c->window < 0) return WMTP_ERR_INVALID_ARG;
+  if (c->window >= 1) {
+    if ((long long)c->sink + c->window != c->capacity) return WMTP_ERR_INVALID_ARG;
+  } else if (c->sink != c->capacity) {
+    return WMTP_ERR_INVALID_ARG;
+  }
+  if (!aligned(c->k, 16) || !aligned(c->v, 16) || !aligned(c->seq_len, 4)) return WMTP_ERR_INVALID_ARG;
+  if (c->pos && !aligned(c->pos, 4)) return WMTP_ERR_INVALID_ARG;
+  return WMTP_OK;
+}
+
+int attention_call(const wmtp_kv* c, const void* q, int m, int n_q_heads, float sm_scale,
+                   int limit, int mode, float* out, float* lse, void* ws, size_t ws_bytes,
+                   void* stream) {
+  if (!q || !out) return WMTP_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4))) return WMTP_ERR_INVALID_ARG;
+  if (n_q_heads < c->n_kv_heads || n_q_heads % c->n_kv_heads) return WMTP_ERR_INVALID_ARG;
+  if (!isfinite(sm_scale)) return WMTP_ERR_INVALID_ARG;
+  SplitPlan plan;
+  if (!wmtp::make_plan_for(c->batch, n_q_heads, c->n_kv_heads, c->head_dim, m, limit, c->dtype,
+                           &plan))
+    return WMTP_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < plan_bytes(plan)) return WMTP_ERR_WORKSPACE;
+
+  wmtp::AttnArgs a;
+  a.q = q;
+  a.k = c->k;
+  a.v = c->v;
+  a.seq_len = c->seq_len;
+  a.out = out;
+  a.lse = lse;
+  a.ws_o = static_cast<float*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                     round_up(plan.ws_o_floats * sizeof(float), kAlign));
+  a.batch = c->batch;
+  a.n_kv_heads = c->n_kv_heads;
+  a.n_q_heads = n_q_heads;
+  a.head_dim = c->head_dim;
+  a.m = m;
+  a.capacity = c->capacity;
+  a.limit = limit;
+  a.mode = mode;
+  a.sm_scale = sm_scale;
+  hipError_t e = wmtp::launch_attention(a, plan, c->dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WMTP_OK : WMTP_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wmtp_ring_append(const wmtp_kv* cache, const void* k_new, const void* v_new, int32_t n_new,
+                     void* stream) {
+  int st = check_kv(cache);
+  if (st != WMTP_OK) return st;
+  if (n_new < 0) return WMTP_ERR_INVALID_ARG;
+  if (n_new == 0) return WMTP_OK;
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return WMTP_ERR_INVALID_ARG;
+  if (cache->window == 0 && n_new > cache->capacity) return WMTP_ERR_CAPACITY;
+  wmtp::AppendArgs a;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.pos = cache->pos;
+  a.seq_len = cache->seq_len;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.batch = cache->batch;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.capacity = cache->capacity;
+  a.sink = cache->sink;
+  a.window = cache->window;
+  a.n_new = n_new;
+  a.elem_bytes = elem_bytes(cache->dtype);
+  hipError_t e = wmtp::launch_append(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WMTP_OK : WMTP_ERR_HIP;
+}
+
+int wmtp_draft_attn_windowed(const wmtp_kv* ring, const void* q, int32_t n_q_heads, float sm_scale,
+                             float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_kv(ring);
+  if (st != WMTP_OK) return st;
+  if (ring->window < 1) return WMTP_ERR_INVALID_ARG;
+  return attention_call(ring, q, 1, n_q_heads, sm_scale, ring->capacity, wmtp::kModeWindowed, out,
+                        lse, ws, ws_bytes, stream);
+}
+
+int wmtp_draft_attn_full(const wmtp_kv* cache, const void* q, int32_t n_q_heads, float sm_scale,
+                         int32_t max_seq_len, float* out, float* lse, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int st = check_kv(cache);
+  if (st != WMTP_OK) return st;
+  if (cache->window != 0) return WMTP_ERR_INVALID_ARG;
+  if (max_seq_len < 1 || max_seq_len > cache->capacity) return WMTP_ERR_INVALID_ARG;
+  return attention_call(cache, q, 1, n_q_heads, sm_scale, max_seq_len, wmtp::kModeFull, out, lse,
+                        ws, ws_bytes, stream);
+}
+
+int wmtp_verify_attn(const wmtp_kv* cache, const void* q, int32_t m, int32_t n_q_heads,
+                     float sm_scale, int32_t max_seq_len, float* out, float* lse, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int st = check_kv(cache);
+  if (st != WMTP_OK) return st;
+  if (cache->window != 0) return WMTP_ERR_INVALID_ARG;
+  if (m < 1 || m > wmtp::kMaxM) return WMTP_ERR_INVALID_ARG;
+  if (max_seq_len < 1 || max_seq_len > cache->capacity) return WMTP_ERR_INVALID_ARG;
+  return attention_call(cache, q, m, n_q_heads, sm_scale, max_seq_len, wmtp::kModeVerify, out, lse,
+                        ws, ws_bytes, stream);
+}
+
+size_t wmtp_attn_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, int32_t m, int32_t max_seq_len) {
+  // the largest need over the supported dtypes, so one size serves every cache
+  size_t best = 0;
+  const int dtypes[2] = {WMTP_F32, WMTP_BF16};
+  for (int dt : dtypes) {
+    SplitPlan p;
+    if (!wmtp::make_plan_for(batch, n_q_heads, n_kv_heads, head_dim, m, max_seq_len, dt, &p))
+      return 0;
+    const size_t bytes = plan_bytes(p);
+    if (bytes > best) best = bytes;
+  }
+  return best;
+}
+
+const char* wmtp_status_string(int status) {
+  switch (status) {
+    case WMTP_OK: return "WMTP_OK";
+    case WMTP_ERR_INVALID_ARG: return "WMTP_ERR_INVALID_ARG: invalid argument";
+    case WMTP_ERR_UNSUPPORTED: return "WMTP_ERR_UNSUPPORTED: dtype or head_dim not implemented";
+    case WMTP_ERR_CAPACITY: return "WMTP_ERR_CAPACITY: request exceeds the cache capacity";
+    case WMTP_ERR_WORKSPACE: return "WMTP_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case WMTP_ERR_HIP: return "WMTP_ERR_HIP: HIP launch error";
+    default: return "unknown wmtp status";
+  }
+}
+
+}  // extern "C"

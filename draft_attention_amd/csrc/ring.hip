@@ -1,0 +1,133 @@
+// ring.hip -- append of new tokens' K/V into a compact ring buffer or a contiguous cache.
+//
+// The compact ring buffer holds what the Windowed-MTP draft reads and nothing else (Windowed-MTP
+// abstract, last sentence: the unread draft KV is reclaimed by a compact ring buffer): S pinned
+// sink slots and W window slots that wrap. Position p lives in slot p if p < S, else in slot
+// S + (p - S) mod W. A contiguous cache is the same map with W = 0 (slot = p).
+//
+// Only survivors are written: of the n_new tokens appended at positions n .. n+n_new-1 of a ring,
+// a token is still held afterwards iff it is a sink (p < S) or one of the last W positions
+// (p >= n + n_new - W); any other token would be overwritten within the same append. So a bulk
+// append never writes one slot twice, and the workgroups of a launch never race on a slot.
+//
+// seq_len[b] is read by every thread that computes slots and advanced by n_new. When one workgroup
+// handles a whole sequence it advances seq_len itself after a barrier (one launch); when a bulk
+// append is spread over many workgroups, a second one-wavefront kernel advances it after the copy.
+
+#include "wmtp_internal.h"
+
+namespace wmtp {
+namespace {
+
+struct Survivors {
+  int64_t n;       // tokens present before the append (>= 0)
+  int64_t first;   // survivors u < first are tokens t = u (sinks appended now)
+  int64_t second;  // survivors u >= first are tokens t = second + (u - first)
+  int64_t count;   // number of survivors
+};
+
+__device__ __forceinline__ Survivors survivors_of(int64_t n, int sink, int window, int capacity,
+                                                  int n_new) {
+  Survivors s;
+  s.n = n;
+  if (window == 0) {
+    // contiguous cache: every token below capacity
+    const int64_t room = capacity > n ? capacity - n : 0;
+    s.first = 0;
+    s.second = 0;
+    s.count = n_new < room ? n_new : room;
+    return s;
+  }
+  int64_t a = sink - n;  // tokens of this append that are sinks
+  if (a < 0) a = 0;
+  if (a > n_new) a = n_new;
+  int64_t w0 = (int64_t)n_new - window;  // first token that is among the last W
+  if (w0 < a) w0 = a;
+  s.first = a;
+  s.second = w0;
+  s.count = a + (n_new - w0);
+  return s;
+}
+
+__device__ __forceinline__ int64_t slot_of(int64_t p, int sink, int window) {
+  if (window == 0 || p < sink) return p;
+  return sink + (p - sink) % window;
+}
+
+// Copy the survivors' rows of sequence b; threads of the x/y grid share the work.
+__device__ __forceinline__ void copy_rows(const AppendArgs& a, int b, const Survivors& sv,
+                                          int64_t tid, int64_t nthreads) {
+  const int chunks = a.head_dim * a.elem_bytes / 16;  // 16-byte pieces per row
+  const int64_t total = sv.count * a.n_kv_heads * chunks;
+  for (int64_t i = tid; i < total; i += nthreads) {
+    const int c = (int)(i % chunks);
+    const int64_t r = i / chunks;
+    const int h = (int)(r % a.n_kv_heads);
+    const int64_t u = r / a.n_kv_heads;
+    const int64_t t = u < sv.first ? u : sv.second + (u - sv.first);
+    const int64_t p = sv.n + t;
+    const int64_t slot = slot_of(p, a.sink, a.window);
+    const size_t src = (((size_t)b * a.n_new + t) * a.n_kv_heads + h) * chunks + c;
+    const size_t dst = (((size_t)b * a.n_kv_heads + h) * a.capacity + slot) * chunks + c;
+    reinterpret_cast<uint4*>(a.k)[dst] = reinterpret_cast<const uint4*>(a.k_new)[src];
+    reinterpret_cast<uint4*>(a.v)[dst] = reinterpret_cast<const uint4*>(a.v_new)[src];
+    if (a.pos && h == 0 && c == 0) a.pos[(size_t)b * a.capacity + slot] = (int32_t)p;
+  }
+}
+
+__device__ __forceinline__ int64_t present(const int32_t* seq_len, int b) {
+  const int32_t n = seq_len[b];
+  return n > 0 ? n : 0;
+}
+
+// One workgroup per sequence: copy, barrier, then advance seq_len (no other workgroup reads it).
+__global__ __launch_bounds__(256) void append_fused_kernel(AppendArgs a) {
+  const int b = blockIdx.x;
+  const int64_t n = present(a.seq_len, b);
+  const Survivors sv = survivors_of(n, a.sink, a.window, a.capacity, a.n_new);
+  copy_rows(a, b, sv, threadIdx.x, blockDim.x);
+  __syncthreads();  // every thread has read seq_len[b] before it changes
+  if (threadIdx.x == 0) {
+    const int64_t next = n + a.n_new;
+    a.seq_len[b] = (int32_t)(next > 0x7fffffffLL ? 0x7fffffffLL : next);
+  }
+}
+
+// Bulk copy over many workgroups per sequence; seq_len is only read here.
+__global__ __launch_bounds__(256) void append_copy_kernel(AppendArgs a) {
+  const int b = blockIdx.y;
+  const int64_t n = present(a.seq_len, b);
+  const Survivors sv = survivors_of(n, a.sink, a.window, a.capacity, a.n_new);
+  copy_rows(a, b, sv, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+            (int64_t)gridDim.x * blockDim.x);
+}
+
+__global__ __launch_bounds__(64) void append_bump_kernel(int32_t* seq_len, int batch, int n_new) {
+  for (int b = threadIdx.x; b < batch; b += blockDim.x) {
+    const int64_t next = present(seq_len, b) + n_new;
+    seq_len[b] = (int32_t)(next > 0x7fffffffLL ? 0x7fffffffLL : next);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+  // host-side bound on the survivors of any sequence
+  const long long max_surv =
+      a.window == 0 ? (a.n_new < a.capacity ? a.n_new : a.capacity)
+                    : (a.n_new < (long long)a.sink + a.window ? a.n_new : (long long)a.sink + a.window);
+  const long long pieces = max_surv * a.n_kv_heads * (a.head_dim * a.elem_bytes / 16);
+  if (pieces <= 256LL * 16) {
+    append_fused_kernel<<<dim3(a.batch), dim3(256), 0, stream>>>(a);
+    return hipGetLastError();
+  }
+  long long blocks = (pieces + 256LL * 8 - 1) / (256LL * 8);
+  if (blocks > 65535) blocks = 65535;
+  append_copy_kernel<<<dim3((unsigned)blocks, a.batch), dim3(256), 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  append_bump_kernel<<<dim3(1), dim3(64), 0, stream>>>(a.seq_len, a.batch, a.n_new);
+  return hipGetLastError();
+}
+
+}  // namespace wmtp

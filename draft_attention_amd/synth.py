@@ -133,3 +133,30 @@ def host_array(t: torch.Tensor):
     if t.dtype == torch.bfloat16:
         return bf16_bits(t)
     return t.detach().cpu().contiguous().numpy()
+
+
+def sequence_rows(seed: int, tensor_id: int, b: int, p0: int, p1: int, n_heads: int, dim: int,
+                  dtype: torch.dtype, device, scale: Optional[float] = None) -> torch.Tensor:
+    """Rows of positions [p0, p1) of sequence b, head-major ``[n_heads][p1-p0][dim]`` in the
+    storage dtype (the layout of one sequence of a KV cache)."""
+    pos = torch.arange(p0, p1, dtype=torch.int64, device=device)
+    x = normal_rows(seed, tensor_id, b, pos, n_heads, dim, device)
+    return cast(x, dtype, scale).permute(1, 0, 2).contiguous()
+
+
+def token_rows(seed: int, tensor_id: int, b: int, p0: int, p1: int, n_heads: int, dim: int,
+               dtype: torch.dtype, device, scale: Optional[float] = None) -> torch.Tensor:
+    """The same rows token-major ``[p1-p0][n_heads][dim]`` (the layout of appended tokens)."""
+    pos = torch.arange(p0, p1, dtype=torch.int64, device=device)
+    return cast(normal_rows(seed, tensor_id, b, pos, n_heads, dim, device), dtype, scale)
+
+
+def queries(seed: int, step: int, batch: int, m: int, n_heads: int, dim: int,
+            dtype: torch.dtype, device) -> torch.Tensor:
+    """Query tensor ``[batch][m][n_heads][dim]`` of draft/verify step ``step``: the m query
+    tokens of sequence b are counter positions step*m .. step*m+m-1 of the Q stream."""
+    out = torch.empty((batch, m, n_heads, dim), dtype=dtype, device=device)
+    for b in range(batch):
+        pos = torch.arange(step * m, step * m + m, dtype=torch.int64, device=device)
+        out[b] = cast(normal_rows(seed, Q_ID, b, pos, n_heads, dim, device), dtype)
+    return out

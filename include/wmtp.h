@@ -1,0 +1,146 @@
+/*
+ * wmtp.h -- C ABI of libwmtp.so: Windowed-MTP draft attention, the full-context draft attention it
+ * replaces, and the target's full-attention verification, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the Windowed-MTP abstract (thelatestinai.com/papers/2607.21535; the same
+ * text is on the khansong-paper-with-me page):
+ *   - a native MTP draft head runs full attention over the entire KV cache at every draft step
+ *     (third sentence)                                      -> wmtp_draft_attn_full
+ *   - the draft may take several steps, each of which appends its token first (fourth sentence)
+ *                                                            -> wmtp_ring_append + an attention call
+ *   - Windowed-MTP gives only the draft's attention a StreamingLLM-style set of attention sinks plus
+ *     a sliding window, leaving full-attention verification intact (fifth sentence)
+ *                                                            -> wmtp_draft_attn_windowed,
+ *                                                               wmtp_verify_attn
+ *   - the draft KV that is never read is reclaimed by a compact ring buffer (last sentence)
+ *                                                            -> the ring layout of wmtp_kv
+ *
+ * Conventions (the pages fix none of them; these are the library's):
+ *   - Positions: the tokens of sequence b are numbered 0, 1, 2, ... in append order; seq_len[b] is
+ *     how many have been appended. Attention sinks are positions 0..sink-1; the window is the last
+ *     `window` positions, the newest included; a position in both sets is attended once.
+ *   - Slot map: position p lives in slot p if p < sink, else in slot sink + (p - sink) % window.
+ *     A contiguous (non-ring) cache is the same descriptor with window = 0 and sink = capacity, so
+ *     that slot(p) = p.
+ *   - GQA: query head hq reads KV head hq / G, G = n_q_heads / n_kv_heads (contiguous groups).
+ *   - Layouts are dense, row-major, C order:
+ *       cache K and V      [batch][n_kv_heads][capacity][head_dim]   (dtype of the cache)
+ *       pos                [batch][capacity] int32                    (optional)
+ *       seq_len            [batch] int32
+ *       new tokens         [batch][n_new][n_kv_heads][head_dim]       (dtype of the cache)
+ *       q                  [batch][m][n_q_heads][head_dim]            (dtype of the cache; m = 1
+ *                                                                      for a draft step)
+ *       out                [batch][m][n_q_heads][head_dim] float32
+ *       lse                [batch][m][n_q_heads] float32, natural log (optional)
+ *   - Scores are sm_scale * (q . k); softmax and all accumulation are float32. bf16 operands are
+ *     multiplied exactly; the softmax weights are rounded to bf16 for the weighted sum of V.
+ *
+ * Ownership and execution: every pointer inside wmtp_kv and every q/out/lse/ws/k_new/v_new pointer
+ * is DEVICE memory owned by the caller. The library never allocates, frees or synchronises; it
+ * keeps no global state, so calls from several host threads are safe. Every call only enqueues work
+ * on `stream` (a hipStream_t; NULL = the null stream) and returns; buffers must stay alive and
+ * unmodified until the stream has passed the call. The wmtp_kv descriptor itself is host memory and
+ * is read only during the call.
+ *
+ * Errors: every entry point validates its host-side arguments first and returns a nonzero
+ * wmtp_status WITHOUT launching anything or touching any buffer when they are invalid. A HIP launch
+ * failure returns WMTP_ERR_HIP. No C++ exception or abort crosses this ABI. Device-side contents
+ * (seq_len, the data) cannot be validated on the host; the kernels never access memory outside the
+ * buffers described, whatever seq_len holds (see each call).
+ */
+#ifndef WMTP_H
+#define WMTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum wmtp_status {
+  WMTP_OK = 0,
+  WMTP_ERR_INVALID_ARG = 1, /* null pointer, inconsistent sizes, bad descriptor */
+  WMTP_ERR_UNSUPPORTED = 2, /* dtype, head_dim or group shape the kernels do not implement */
+  WMTP_ERR_CAPACITY = 3,    /* a request that cannot fit (n_new larger than a contiguous cache) */
+  WMTP_ERR_WORKSPACE = 4,   /* workspace missing or smaller than wmtp_attn_workspace_bytes */
+  WMTP_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
+} wmtp_status;
+
+typedef enum wmtp_dtype { WMTP_F32 = 0, WMTP_BF16 = 1 } wmtp_dtype;
+
+/* A KV cache of `batch` sequences: a compact ring buffer (window >= 1, capacity = sink + window) or
+ * a contiguous cache (window = 0, sink = capacity). head_dim must be 64, 128 or 256. */
+typedef struct wmtp_kv {
+  void* k;          /* device [batch][n_kv_heads][capacity][head_dim] */
+  void* v;          /* device [batch][n_kv_heads][capacity][head_dim] */
+  int32_t* pos;     /* device [batch][capacity]: position held by each slot, or NULL */
+  int32_t* seq_len; /* device [batch]: tokens appended so far */
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t capacity;
+  int32_t sink;
+  int32_t window;
+  int32_t dtype; /* wmtp_dtype */
+} wmtp_kv;
+
+/* Append n_new tokens to every sequence (the k_new/v_new rows of sequence b get positions
+ * seq_len[b] .. seq_len[b] + n_new - 1), then seq_len[b] += n_new, all on `stream`.
+ * For each token, K and V of every KV head are copied bit for bit into slot(p), and pos[b][slot]
+ * is set to p when pos is not NULL. In a ring, only the tokens that are still held after the
+ * append are written (sinks, and the last `window` positions), so a bulk append of any size writes
+ * each slot at most once. In a contiguous cache, tokens whose position would reach `capacity` are
+ * not written (seq_len still advances; the caller's contract is seq_len[b] + n_new <= capacity,
+ * which the device cannot report).
+ * Errors: INVALID_ARG (null pointers, n_new < 0, bad descriptor), UNSUPPORTED (dtype, head_dim),
+ * CAPACITY (contiguous cache with n_new > capacity), HIP. n_new = 0 is a no-op returning WMTP_OK. */
+int wmtp_ring_append(const wmtp_kv* cache, const void* k_new, const void* v_new, int32_t n_new,
+                     void* stream);
+
+/* Windowed-MTP draft step: one query token per sequence (q is [batch][1][n_q_heads][head_dim])
+ * attends the occupied slots of its ring, which hold exactly the sink positions and the last
+ * `window` positions: c_b = min(seq_len[b], capacity) slots, 0..c_b-1. `ring` must be a ring
+ * (window >= 1). out is [batch][1][n_q_heads][head_dim] float32; lse (nullable) [batch][1][n_q_heads].
+ * A sequence with seq_len[b] <= 0 gets out = 0 and lse = -inf.
+ * ws: device workspace of at least
+ *   wmtp_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, 1, capacity) bytes.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+int wmtp_draft_attn_windowed(const wmtp_kv* ring, const void* q, int32_t n_q_heads, float sm_scale,
+                             float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Native full-context draft step: one query token per sequence attends every cached position
+ * 0..n_b-1 of a contiguous cache (window == 0), n_b = min(seq_len[b], capacity). max_seq_len is a
+ * host-side upper bound on every seq_len[b] (1 <= max_seq_len <= capacity), used only to size the
+ * launch; positions at or beyond max_seq_len are never read. out/lse as for the windowed call.
+ * ws: at least wmtp_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, 1, max_seq_len).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+int wmtp_draft_attn_full(const wmtp_kv* cache, const void* q, int32_t n_q_heads, float sm_scale,
+                         int32_t max_seq_len, float* out, float* lse, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Target verification of m draft candidates with full attention: the candidates are the last m
+ * cached positions n_b-m .. n_b-1 of a contiguous cache (window == 0), and candidate j attends
+ * positions 0 .. n_b-m+j (the prefix plus candidates 0..j). q is [batch][m][n_q_heads][head_dim];
+ * out [batch][m][n_q_heads][head_dim] float32; lse (nullable) [batch][m][n_q_heads]. A candidate
+ * with no visible position (n_b-m+j < 0) gets out = 0 and lse = -inf. 1 <= m <= 16.
+ * ws: at least wmtp_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, m, max_seq_len).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+int wmtp_verify_attn(const wmtp_kv* cache, const void* q, int32_t m, int32_t n_q_heads,
+                     float sm_scale, int32_t max_seq_len, float* out, float* lse, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Workspace bytes an attention call with these sizes needs (split-K partial results). Pass
+ * m = 1 for draft steps and max_seq_len = capacity for the windowed call. Depends only on its
+ * arguments (not on the device). Returns 0 for arguments no attention call accepts. */
+size_t wmtp_attn_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, int32_t m, int32_t max_seq_len);
+
+/* Static, human-readable name of a wmtp_status value (never NULL). */
+const char* wmtp_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WMTP_H */

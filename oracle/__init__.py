@@ -195,13 +195,20 @@ class LogicalKV:
                 return first_row + (p0 - first_pos), p1 - p0
         raise KeyError(f"positions [{p0},{p1}) of sequence {b} are not held as one run")
 
+    def row_indices(self, b: int, positions: np.ndarray) -> np.ndarray:
+        """Row holding each position of sequence b (KeyError if one is not held)."""
+        positions = np.asarray(positions, dtype=np.int64)
+        rows = np.full(positions.shape, -1, dtype=np.int64)
+        for first_pos, first_row, count in self.segments[b]:
+            inside = (positions >= first_pos) & (positions < first_pos + count)
+            rows[inside] = first_row + (positions[inside] - first_pos)
+        if np.any(rows < 0):
+            raise KeyError(f"positions {positions[rows < 0][:4]} of sequence {b} are not held")
+        return rows
+
     def rows_of_positions(self, b: int, h: int, positions: np.ndarray, which: str = "k"):
         arr = self.k if which == "k" else self.v
-        out = np.empty((len(positions), arr.shape[-1]), dtype=arr.dtype)
-        for i, p in enumerate(positions):
-            r, _ = self.row_run(b, int(p), int(p) + 1)
-            out[i] = arr[b, h, r]
-        return out
+        return arr[b, h, self.row_indices(b, positions)]
 
 
 def contiguous_kv(k: np.ndarray, v: np.ndarray, dtype: int) -> LogicalKV:

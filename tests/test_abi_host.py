@@ -1,0 +1,134 @@
+"""The C ABI on the host (no GPU): libwmtp.so loads, exports every function include/wmtp.h
+declares, and every invalid argument is refused with its status before anything is launched."""
+import ctypes
+import math
+import os
+
+import pytest
+
+from draft_attention_amd import binding as W
+
+FAKE = 0x10000  # an aligned, non-null address that is never dereferenced (validation fails first)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(W.LIB_PATH):
+        from draft_attention_amd import build
+
+        build.build()
+    return W.lib()
+
+
+def _kv(**kw):
+    base = dict(k=FAKE, v=FAKE, pos=None, seq_len=FAKE, batch=2, n_kv_heads=2, head_dim=128,
+                capacity=20, sink=4, window=16, dtype=W.WMTP_BF16)
+    base.update(kw)
+    return W.wmtp_kv(**base)
+
+
+def test_exports_every_declared_function(lib):
+    names = W.header_functions()
+    assert set(names) == {"wmtp_ring_append", "wmtp_draft_attn_windowed", "wmtp_draft_attn_full",
+                          "wmtp_verify_attn", "wmtp_attn_workspace_bytes", "wmtp_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for st in range(6):
+        assert W.status_string(st).startswith("WMTP_")
+    assert "unknown" in W.status_string(99)
+
+
+def _append(desc, k_new=FAKE, v_new=FAKE, n_new=1):
+    return W.lib().wmtp_ring_append(ctypes.byref(desc) if desc is not None else None, k_new,
+                                    v_new, n_new, None)
+
+
+def _windowed(desc, q=FAKE, hq=8, scale=0.1, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return W.lib().wmtp_draft_attn_windowed(ctypes.byref(desc), q, hq, scale, out, None, ws,
+                                            ws_bytes, None)
+
+
+def _full(desc, bound=10, hq=8, ws_bytes=1 << 30, ws=FAKE):
+    return W.lib().wmtp_draft_attn_full(ctypes.byref(desc), FAKE, hq, 0.1, bound, FAKE, None, ws,
+                                        ws_bytes, None)
+
+
+def _verify(desc, m=4, bound=10, hq=8, ws_bytes=1 << 30):
+    return W.lib().wmtp_verify_attn(ctypes.byref(desc), FAKE, m, hq, 0.1, bound, FAKE, None, FAKE,
+                                    ws_bytes, None)
+
+
+CONTIG = dict(capacity=64, sink=64, window=0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), W.WMTP_ERR_UNSUPPORTED),
+    (dict(head_dim=96), W.WMTP_ERR_UNSUPPORTED),
+    (dict(k=None), W.WMTP_ERR_INVALID_ARG),
+    (dict(v=None), W.WMTP_ERR_INVALID_ARG),
+    (dict(seq_len=None), W.WMTP_ERR_INVALID_ARG),
+    (dict(batch=0), W.WMTP_ERR_INVALID_ARG),
+    (dict(n_kv_heads=0), W.WMTP_ERR_INVALID_ARG),
+    (dict(capacity=21), W.WMTP_ERR_INVALID_ARG),          # ring: capacity != sink + window
+    (dict(sink=-1, capacity=15), W.WMTP_ERR_INVALID_ARG),
+    (dict(capacity=64, sink=60, window=0), W.WMTP_ERR_INVALID_ARG),  # contiguous: sink != cap
+    (dict(k=FAKE + 8), W.WMTP_ERR_INVALID_ARG),           # misaligned
+    (dict(pos=FAKE + 2), W.WMTP_ERR_INVALID_ARG),
+])
+def test_descriptor_validation(lib, kw, status):
+    d = _kv(**kw)
+    assert _append(d) == status
+    assert _windowed(d) == status
+
+
+def test_append_validation(lib):
+    assert lib.wmtp_ring_append(None, FAKE, FAKE, 1, None) == W.WMTP_ERR_INVALID_ARG
+    assert _append(_kv(), n_new=-1) == W.WMTP_ERR_INVALID_ARG
+    assert _append(_kv(), n_new=0) == W.WMTP_OK  # no-op, nothing launched
+    assert _append(_kv(), k_new=None) == W.WMTP_ERR_INVALID_ARG
+    assert _append(_kv(), v_new=FAKE + 4) == W.WMTP_ERR_INVALID_ARG
+    assert _append(_kv(**CONTIG), n_new=65) == W.WMTP_ERR_CAPACITY
+
+
+def test_windowed_validation(lib):
+    need = W.wmtp_attn_workspace_bytes(2, 8, 2, 128, 1, 20)
+    assert need > 0
+    assert _windowed(_kv(**CONTIG)) == W.WMTP_ERR_INVALID_ARG       # not a ring
+    assert _windowed(_kv(), hq=7) == W.WMTP_ERR_INVALID_ARG          # Hq % Hkv != 0
+    assert _windowed(_kv(), hq=1) == W.WMTP_ERR_INVALID_ARG          # Hq < Hkv
+    assert _windowed(_kv(), q=None) == W.WMTP_ERR_INVALID_ARG
+    assert _windowed(_kv(), out=None) == W.WMTP_ERR_INVALID_ARG
+    assert _windowed(_kv(), out=FAKE + 4) == W.WMTP_ERR_INVALID_ARG
+    assert _windowed(_kv(), scale=math.nan) == W.WMTP_ERR_INVALID_ARG
+    assert _windowed(_kv(), ws=None) == W.WMTP_ERR_WORKSPACE
+    assert _windowed(_kv(), ws=FAKE + 16) == W.WMTP_ERR_WORKSPACE    # not 256-byte aligned
+    assert _windowed(_kv(), ws_bytes=need - 1) == W.WMTP_ERR_WORKSPACE
+
+
+def test_full_and_verify_validation(lib):
+    c = _kv(**CONTIG)
+    assert _full(_kv()) == W.WMTP_ERR_INVALID_ARG                    # a ring is not a full cache
+    assert _full(c, bound=0) == W.WMTP_ERR_INVALID_ARG
+    assert _full(c, bound=65) == W.WMTP_ERR_INVALID_ARG              # beyond capacity
+    assert _full(c, ws_bytes=16) == W.WMTP_ERR_WORKSPACE
+    assert _verify(c, m=0) == W.WMTP_ERR_INVALID_ARG
+    assert _verify(c, m=17) == W.WMTP_ERR_INVALID_ARG
+    assert _verify(_kv()) == W.WMTP_ERR_INVALID_ARG
+    assert _verify(c, ws_bytes=16) == W.WMTP_ERR_WORKSPACE
+
+
+def test_workspace_bytes(lib):
+    f = W.wmtp_attn_workspace_bytes
+    assert f(1, 8, 2, 96, 1, 100) == 0          # unsupported head_dim
+    assert f(1, 7, 2, 128, 1, 100) == 0         # Hq % Hkv
+    assert f(1, 8, 2, 128, 0, 100) == 0         # m < 1
+    assert f(1, 8, 2, 128, 17, 100) == 0        # m > 16
+    assert f(1, 8, 2, 128, 1, 0) == 0
+    small, big = f(1, 32, 2, 256, 1, 4100), f(1, 32, 2, 256, 1, 1048581)
+    assert 0 < small <= big
+    # the split-K partials stay a small fraction of the K/V bytes a full 1M-token read streams
+    kv_bytes = 2 * 2 * 1048581 * 256 * 2
+    assert big < 0.05 * kv_bytes

@@ -1,0 +1,245 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64 oracle, at sizes the oracle
+finishes in seconds: several 16-key tiles, several splits, ragged tails, and the edge cases of
+the sink/window/causal sets. Ring contents and position tags must match bit for bit."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from draft_attention_amd import binding as W
+from draft_attention_amd import synth
+from gpu_common import (DEV, TOL, append_all, append_each, compare, logical_kv, ocode,
+                        oracle_kv, run_full, run_verify, run_windowed, say, select, tdtype)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_ring(ring: W.KVCache, model: oracle.RingModel, kv: oracle.LogicalKV, what: str):
+    tags = ring.pos.cpu().numpy().astype(np.int64)
+    assert np.array_equal(tags, model.tags), f"{what}: position tags differ"
+    assert np.array_equal(ring.seq_len.cpu().numpy().astype(np.int64), model.n), f"{what}: seq_len"
+    rk, rv = oracle.ring_expected(model, kv)
+    hk, hv = synth.host_array(ring.k), synth.host_array(ring.v)
+    for b in range(ring.batch):
+        occ = model.occupied_slots(b)
+        assert np.array_equal(hk[b][:, occ], rk[b][:, occ]), f"{what}: K bytes of sequence {b}"
+        assert np.array_equal(hv[b][:, occ], rv[b][:, occ]), f"{what}: V bytes of sequence {b}"
+
+
+# ------------------------------------------------------------------------------------------
+# ring append: bit-exact against the host ring model
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("S,Wn", [(4, 16), (0, 7), (3, 1), (4, 256)])
+def test_ring_append_bitexact(dt, d, S, Wn):
+    B, Hkv = 3, 2
+    say(f"ring append {dt} d={d} S={S} W={Wn}")
+    total = 3 * (S + Wn) + 700
+    K, V = logical_kv(11, B, Hkv, d, total, tdtype(dt))
+    kv = oracle_kv(K, V, dt)
+    ring = W.KVCache.ring(B, Hkv, d, S, Wn, tdtype(dt))
+    model = oracle.RingModel(B, S, Wn)
+    lens = [0] * B
+    # ragged prefixes (one call per sequence), then common appends of assorted sizes
+    first = [1, S + Wn + 5, 2 * (S + Wn) + 3]
+    append_each(ring, K, V, lens, first)
+    for b, t in enumerate(first):
+        model.append(b, t)
+        lens[b] += t
+    _check_ring(ring, model, kv, "after ragged prefill")
+    for t in [1, 1, 3, Wn + 2, 1, S + 1, 2 * Wn + 7, 1]:
+        if max(lens) + t > total:
+            break
+        append_all(ring, K, V, lens, t)
+        for b in range(B):
+            model.append(b, t)
+            lens[b] += t
+        _check_ring(ring, model, kv, f"after append of {t}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_contiguous_append_and_overflow(dt):
+    B, Hkv, d, cap = 2, 2, 128, 300
+    say(f"contiguous append {dt}")
+    K, V = logical_kv(12, B, Hkv, d, cap + 40, tdtype(dt))
+    cache = W.KVCache.contiguous(B, Hkv, d, cap, tdtype(dt), with_pos=True)
+    append_each(cache, K, V, [0, 0], [250, 17])
+    append_all(cache, K, V, [250, 17], 30)  # sequence 0 reaches 280 of 300
+    append_all(cache, K, V, [280, 47], 30)  # sequence 0 would reach 310: positions >= 300 dropped
+    torch.cuda.synchronize()
+    n = cache.seq_len.cpu().tolist()
+    assert n == [310, 77]
+    hk = synth.host_array(cache.k)
+    exp = synth.host_array(K)
+    assert np.array_equal(hk[0][:, :cap], exp[0][:, :cap])  # positions >= capacity dropped
+    assert np.array_equal(hk[1][:, :77], exp[1][:, :77])
+    pos = cache.pos.cpu().numpy()
+    assert np.array_equal(pos[0], np.arange(cap))
+    assert np.array_equal(pos[1][:77], np.arange(77)) and np.all(pos[1][77:] == -1)
+    # the API refuses a single append larger than a contiguous cache
+    kn = torch.zeros((B, cap + 1, Hkv, d), dtype=tdtype(dt), device=DEV)
+    assert W.wmtp_ring_append(cache, kn, kn, cap + 1, check=False) == W.WMTP_ERR_CAPACITY
+
+
+# ------------------------------------------------------------------------------------------
+# windowed draft attention over the ring vs the oracle over the logical sequence
+# ------------------------------------------------------------------------------------------
+WIN_CASES = [
+    # dt, d, Hq, Hkv, S, W, lens (ragged batch)
+    ("f32", 64, 8, 2, 4, 256, [1, 3, 4, 5]),
+    ("f32", 64, 8, 2, 4, 256, [259, 260, 261, 1000]),
+    ("f32", 128, 4, 4, 0, 33, [1, 32, 33, 34, 500]),
+    ("f32", 256, 16, 2, 2, 64, [65, 66, 67, 900]),
+    ("bf16", 64, 4, 1, 4, 100, [3, 104, 105, 333]),
+    ("bf16", 128, 32, 4, 4, 2048, [2051, 2052, 2053, 6000]),
+    ("bf16", 128, 16, 2, 1, 1, [1, 2, 3, 50]),
+    ("bf16", 256, 32, 2, 4, 512, [100, 516, 517, 3000]),
+    ("bf16", 128, 48, 3, 4, 64, [70, 68]),
+]
+
+
+@pytest.mark.parametrize("dt,d,Hq,Hkv,S,Wn,lens", WIN_CASES)
+def test_windowed_parity(dt, d, Hq, Hkv, S, Wn, lens):
+    B = len(lens)
+    say(f"windowed {dt} d={d} Hq={Hq} Hkv={Hkv} S={S} W={Wn} lens={lens}")
+    K, V = logical_kv(21, B, Hkv, d, max(lens), tdtype(dt))
+    ring = W.KVCache.ring(B, Hkv, d, S, Wn, tdtype(dt))
+    # prefill all but the last token per sequence, then append one draft token to all
+    pre = [n - 1 for n in lens]
+    append_each(ring, K, V, [0] * B, pre)
+    append_all(ring, K, V, pre, 1)
+    q = synth.queries(22, 0, B, 1, Hq, d, tdtype(dt), DEV)
+    scale = 1.0 / math.sqrt(d)
+    out, lse = run_windowed(ring, q, Hq, scale)
+    ref_o, ref_l = oracle.draft_windowed(synth.host_array(q), ocode(dt), oracle_kv(K, V, dt), lens,
+                                         S, Wn, scale)
+    compare(out, lse, ref_o, ref_l, dt, "windowed")
+
+
+# ------------------------------------------------------------------------------------------
+# full draft attention over a contiguous cache
+# ------------------------------------------------------------------------------------------
+FULL_CASES = [
+    ("f32", 64, 8, 2, [1, 15, 16, 17, 4097]),
+    ("f32", 128, 8, 8, [33, 1000]),
+    ("f32", 256, 4, 1, [5000]),
+    ("bf16", 64, 16, 2, [7, 999]),
+    ("bf16", 128, 32, 4, [1, 2049, 7777]),
+    ("bf16", 256, 32, 2, [12345, 300]),
+    ("bf16", 128, 8, 8, [64, 65]),
+]
+
+
+@pytest.mark.parametrize("dt,d,Hq,Hkv,lens", FULL_CASES)
+def test_full_parity(dt, d, Hq, Hkv, lens):
+    B = len(lens)
+    say(f"full {dt} d={d} Hq={Hq} Hkv={Hkv} lens={lens}")
+    cap = max(lens) + 37
+    K, V = logical_kv(31, B, Hkv, d, max(lens), tdtype(dt))
+    cache = W.KVCache.contiguous(B, Hkv, d, cap, tdtype(dt))
+    append_each(cache, K, V, [0] * B, lens)
+    q = synth.queries(32, 0, B, 1, Hq, d, tdtype(dt), DEV)
+    scale = 1.0 / math.sqrt(d)
+    ref_o, ref_l = oracle.draft_full(synth.host_array(q), ocode(dt), oracle_kv(K, V, dt), lens,
+                                     scale)
+    # the host bound only sizes the launch: any bound >= every length gives the same result
+    for bound in sorted({max(lens), cap}):
+        out, lse = run_full(cache, q, Hq, scale, bound)
+        compare(out, lse, ref_o, ref_l, dt, f"full (max_seq_len={bound})")
+
+
+def test_full_bound_below_length_reads_nothing_beyond():
+    """max_seq_len < seq_len: keys at or past the bound are never read (result = prefix)."""
+    dt, d, Hq, Hkv, n, bound = "bf16", 128, 8, 2, 900, 700
+    say("full with a short host bound")
+    K, V = logical_kv(33, 1, Hkv, d, n, tdtype(dt))
+    cache = W.KVCache.contiguous(1, Hkv, d, n, tdtype(dt))
+    append_each(cache, K, V, [0], [n])
+    q = synth.queries(34, 0, 1, 1, Hq, d, tdtype(dt), DEV)
+    out, lse = run_full(cache, q, Hq, 0.1, bound)
+    ref_o, ref_l = oracle.draft_full(synth.host_array(q), ocode(dt), oracle_kv(K, V, dt), [bound],
+                                     0.1)
+    compare(out, lse, ref_o, ref_l, dt, "full clamped to the bound")
+
+
+# ------------------------------------------------------------------------------------------
+# verification: m candidates, causal among themselves
+# ------------------------------------------------------------------------------------------
+VERIFY_CASES = [
+    ("bf16", 128, 32, 2, 4, [5000, 64]),
+    ("bf16", 128, 16, 2, 1, [300]),
+    ("bf16", 64, 8, 2, 6, [777, 6]),
+    ("bf16", 256, 16, 2, 2, [1500]),
+    ("bf16", 256, 32, 2, 3, [900]),   # 48 rows: two row chunks
+    ("bf16", 256, 32, 2, 6, [901]),   # 96 rows: three row chunks
+    ("f32", 64, 8, 2, 4, [4097, 2]),
+    ("f32", 128, 8, 1, 3, [999]),
+    ("bf16", 128, 8, 4, 16, [2000]),
+]
+
+
+@pytest.mark.parametrize("dt,d,Hq,Hkv,m,lens", VERIFY_CASES)
+def test_verify_parity(dt, d, Hq, Hkv, m, lens):
+    B = len(lens)
+    say(f"verify {dt} d={d} Hq={Hq} Hkv={Hkv} m={m} lens={lens}")
+    K, V = logical_kv(41, B, Hkv, d, max(lens), tdtype(dt))
+    cache = W.KVCache.contiguous(B, Hkv, d, max(lens) + 8, tdtype(dt))
+    append_each(cache, K, V, [0] * B, lens)
+    q = synth.queries(42, 0, B, m, Hq, d, tdtype(dt), DEV)
+    scale = 1.0 / math.sqrt(d)
+    out, lse = run_verify(cache, q, Hq, scale, max(lens))
+    ref_o, ref_l = oracle.verify(synth.host_array(q), ocode(dt), oracle_kv(K, V, dt), lens, scale)
+    compare(out, lse, ref_o, ref_l, dt, "verify")
+
+
+# ------------------------------------------------------------------------------------------
+# properties that hold on the device
+# ------------------------------------------------------------------------------------------
+def test_windowed_equals_full_when_window_covers_all():
+    dt, d, Hq, Hkv, S, Wn, n = "f32", 64, 8, 2, 4, 256, 257
+    say("windowed == full at S+W >= n")
+    K, V = logical_kv(51, 1, Hkv, d, n, tdtype(dt))
+    ring = W.KVCache.ring(1, Hkv, d, S, Wn, tdtype(dt))
+    cache = W.KVCache.contiguous(1, Hkv, d, n, tdtype(dt))
+    append_each(ring, K, V, [0], [n])
+    append_each(cache, K, V, [0], [n])
+    q = synth.queries(52, 0, 1, 1, Hq, d, tdtype(dt), DEV)
+    ow, lw = run_windowed(ring, q, Hq, 0.125)
+    of, lf = run_full(cache, q, Hq, 0.125, n)
+    assert torch.max(torch.abs(ow - of)).item() <= TOL[dt]
+    assert torch.max(torch.abs(lw - lf)).item() <= TOL[dt]
+
+
+def test_deterministic():
+    dt, d, Hq, Hkv, n = "bf16", 128, 32, 2, 20000
+    say("determinism")
+    K, V = logical_kv(61, 1, Hkv, d, n, tdtype(dt))
+    cache = W.KVCache.contiguous(1, Hkv, d, n, tdtype(dt))
+    append_each(cache, K, V, [0], [n])
+    q = synth.queries(62, 0, 1, 4, Hq, d, tdtype(dt), DEV)
+    a = run_verify(cache, q, Hq, 0.1, n)
+    b = run_verify(cache, q, Hq, 0.1, n)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_empty_sequences_give_zero_and_minus_inf():
+    dt, d, Hq, Hkv = "bf16", 128, 8, 2
+    say("empty sequences")
+    ring = W.KVCache.ring(2, Hkv, d, 4, 16, tdtype(dt))
+    q = synth.queries(71, 0, 2, 1, Hq, d, tdtype(dt), DEV)
+    out, lse = run_windowed(ring, q, Hq, 0.1)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    cache = W.KVCache.contiguous(2, Hkv, d, 64, tdtype(dt))
+    K, V = logical_kv(72, 2, Hkv, d, 2, tdtype(dt))
+    append_each(cache, K, V, [0, 0], [0, 2])  # sequence 0 stays empty, sequence 1 holds 2 tokens
+    qv = synth.queries(73, 0, 2, 4, Hq, d, tdtype(dt), DEV)
+    out, lse = run_verify(cache, qv, Hq, 0.1, 64)
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    # sequence 1: candidates 0 and 1 see nothing (positions -2, -1), 2 and 3 see 1 and 2 tokens
+    assert torch.all(out[1, :2] == 0) and torch.all(torch.isneginf(lse[1, :2]))
+    ref_o, ref_l = oracle.verify(synth.host_array(qv[1:]), ocode(dt), oracle_kv(K[1:], V[1:], dt),
+                                 [2], 0.1)
+    compare(out[1:], lse[1:], ref_o, ref_l, dt, "verify with n < m")

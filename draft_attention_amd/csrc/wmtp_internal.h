@@ -10,7 +10,7 @@
 namespace wmtp {
 
 // Work split of one attention call (split-K flash decoding). Every (sequence, KV head, row chunk)
-// is cut into n_splits key ranges of keys_per_split keys; one wavefront owns one key range and
+// is cut into n_splits key ranges of keys_per_split keys; one workgroup owns one key range and
 // leaves an un-normalised partial result (o, running max, running sum) in the workspace, which a
 // second kernel merges with the log-sum-exp rule. The plan depends only on the call's sizes.
 struct SplitPlan {
@@ -26,8 +26,8 @@ struct SplitPlan {
 };
 
 constexpr int kTileKeys = 16;       // keys per MFMA tile
-constexpr int kWavesPerBlock = 4;   // wavefronts per workgroup (each an independent split)
-constexpr int kTargetWaves = 2048;  // 256 CUs x 8 resident wavefronts
+constexpr int kWavesPerBlock = 4;   // wavefronts per workgroup (interleaved tiles of one range)
+constexpr int kTargetBlocks = 512;  // about two workgroups per CU (256 CUs)
 constexpr int kMaxM = 16;           // verify candidates per call
 
 // Plan for a cache of `dtype`; false when no attention call accepts these sizes.

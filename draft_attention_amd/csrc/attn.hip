@@ -36,9 +36,21 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+
+// K and V are streamed once per call: nontemporal loads keep them from displacing useful lines in
+// the caches (measured on MI355X: the full 1M-token read goes from 6.0 to 6.7 TB/s).
+__device__ __forceinline__ uint4 stream_load16(const void* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(static_cast<const u32x4_t*>(p)));
+}
+__device__ __forceinline__ uint2 stream_load8(const void* p) {
+  return __builtin_bit_cast(uint2, __builtin_nontemporal_load(static_cast<const u32x2_t*>(p)));
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleLog2 = 8.f;  // softmax weights stay below 2^8 between rescales
 constexpr int kThreads = 64 * kWavesPerBlock;
 
 __device__ __forceinline__ float xgroup_max(float x) {
@@ -86,7 +98,7 @@ __device__ __forceinline__ void load_tile(const char* kbase, const char* vbase, 
   const int key = min(t0 + r16, last);
   const uint4* kp = reinterpret_cast<const uint4*>(kbase + (size_t)key * D * F::kEB);
 #pragma unroll
-  for (int ks = 0; ks < F::kQRegs; ++ks) T.k[ks] = kp[ks * 4 + grp];
+  for (int ks = 0; ks < F::kQRegs; ++ks) T.k[ks] = stream_load16(kp + ks * 4 + grp);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int kv = min(t0 + 4 * grp + t, last);
@@ -94,25 +106,45 @@ __device__ __forceinline__ void load_tile(const char* kbase, const char* vbase, 
 #pragma unroll
     for (int st = 0; st < F::kSets; ++st) {
       if constexpr (F::kVWords == 4) {
-        const uint4 x = *reinterpret_cast<const uint4*>(vp + st * F::kSetDims * F::kEB);
+        const uint4 x = stream_load16(vp + st * F::kSetDims * F::kEB);
         T.v[t][st][0] = x.x; T.v[t][st][1] = x.y; T.v[t][st][2] = x.z; T.v[t][st][3] = x.w;
       } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(vp + st * F::kSetDims * F::kEB);
+        const uint2 x = stream_load8(vp + st * F::kSetDims * F::kEB);
         T.v[t][st][0] = x.x; T.v[t][st][1] = x.y;
       }
     }
   }
 }
 
+// The query operand of S^T = K . Q^T for this lane: fragment (rb, ks) holds row rb*16 + (lane & 15),
+// dims ks*32 + (lane >> 4)*8 .. +7 (bf16) or ks*16 + (lane >> 4)*4 .. +3 (fp32). It lives either in
+// registers or, when it would crowd out the K/V tiles, in LDS (read back once per tile; consecutive
+// lanes read consecutive 16 bytes, so the reads are conflict-free).
+template <int D, int NR, bool BF16>
+struct QOperand {
+  using F = Frag<D, BF16>;
+  typedef typename std::conditional<BF16, bf16x8_t, f32x4_t>::type Vec;
+  static constexpr bool kInLds = NR * F::kQRegs * 4 >= 64;
+  Vec reg[kInLds ? 1 : NR][kInLds ? 1 : F::kQRegs];
+  const uint4* lds;
+  int lane;
+  __device__ __forceinline__ Vec get(int rb, int ks) const {
+    if constexpr (kInLds)
+      return __builtin_bit_cast(Vec, lds[(rb * F::kQRegs + ks) * 64 + lane]);
+    else
+      return reg[rb][ks];
+  }
+};
+
 template <int D, int NR, bool BF16>
 struct RowState {
-  float m[NR];  // running max (log2 units), equal on the four lanes of a row
+  float m[NR];  // reference max (log2 units, within 2^8 of the running max), same on a row's lanes
   float l[NR];  // this lane's share of the running sum
   f32x4_t o[NR][Frag<D, BF16>::kBlocks];
 };
 
-template <int D, int NR, bool BF16, typename QVec>
-__device__ __forceinline__ void compute_tile(const Tile<D, BF16>& T, const QVec (&qf)[NR][Frag<D, BF16>::kQRegs],
+template <int D, int NR, bool BF16>
+__device__ __forceinline__ void compute_tile(const Tile<D, BF16>& T, const QOperand<D, NR, BF16>& qf,
                                              int t0, int last, const int (&last_visible)[NR],
                                              int grp, float scale_log2, RowState<D, NR, BF16>& st) {
   using F = Frag<D, BF16>;
@@ -126,48 +158,67 @@ __device__ __forceinline__ void compute_tile(const Tile<D, BF16>& T, const QVec 
 #pragma unroll
       for (int rb = 0; rb < NR; ++rb)
         s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, T.k[ks]),
-                                                        qf[rb][ks], s[rb], 0, 0, 0);
+                                                        qf.get(rb, ks), s[rb], 0, 0, 0);
   } else {
 #pragma unroll
     for (int ks = 0; ks < F::kQRegs; ++ks) {
       const float4 kf = __builtin_bit_cast(float4, T.k[ks]);
 #pragma unroll
       for (int rb = 0; rb < NR; ++rb) {
-        s[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.x, qf[rb][ks][0], s[rb], 0, 0, 0);
-        s[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.y, qf[rb][ks][1], s[rb], 0, 0, 0);
-        s[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.z, qf[rb][ks][2], s[rb], 0, 0, 0);
-        s[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.w, qf[rb][ks][3], s[rb], 0, 0, 0);
+        const f32x4_t q4 = qf.get(rb, ks);
+        s[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.x, q4[0], s[rb], 0, 0, 0);
+        s[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.y, q4[1], s[rb], 0, 0, 0);
+        s[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.z, q4[2], s[rb], 0, 0, 0);
+        s[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.w, q4[3], s[rb], 0, 0, 0);
       }
     }
   }
 
-  // ---------------- online softmax; this lane holds keys t0 + 4*grp + j (j = 0..3) of its row
-  float p[NR][4];
+  // ---------------- online softmax; this lane holds keys t0 + 4*grp + j (j = 0..3) of its row.
+  // The weights are taken relative to a reference maximum st.m that only moves when a tile's
+  // maximum exceeds it by more than kRescaleLog2 (softmax does not depend on the reference), so
+  // the weights stay below 2^kRescaleLog2 and the O accumulators are rescaled only on the rare
+  // tiles where some row's reference moves (a wavefront-uniform branch).
+  float sc[NR][4];
+  bool need = false;
+  float mx[NR];
 #pragma unroll
   for (int rb = 0; rb < NR; ++rb) {
     const int vis = min(last, last_visible[rb]);
-    float sc[4];
-    float mx = -INFINITY;
+    float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = t0 + 4 * grp + j;
-      sc[j] = (key <= vis) ? s[rb][j] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sc[j]);
+      sc[rb][j] = (key <= vis) ? s[rb][j] * scale_log2 : -INFINITY;
+      m = fmaxf(m, sc[rb][j]);
     }
-    mx = xgroup_max(mx);
-    const float m_new = fmaxf(st.m[rb], mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(st.m[rb] - m_use);
+    mx[rb] = xgroup_max(m);
+    need |= mx[rb] > st.m[rb] + kRescaleLog2;
+  }
+  if (__ballot(need)) {
+#pragma unroll
+    for (int rb = 0; rb < NR; ++rb) {
+      // rows whose reference stays put keep alpha = 1 exactly (their st.m may still be -inf
+      // when the causal mask hid every key so far, and -inf - -inf is not a number)
+      const bool moved = mx[rb] > st.m[rb] + kRescaleLog2;
+      const float alpha = moved ? __builtin_amdgcn_exp2f(st.m[rb] - mx[rb]) : 1.f;  // 0 from -inf
+      st.l[rb] *= alpha;
+#pragma unroll
+      for (int i = 0; i < F::kBlocks; ++i) st.o[rb][i] *= alpha;
+      st.m[rb] = moved ? mx[rb] : st.m[rb];
+    }
+  }
+  float p[NR][4];
+#pragma unroll
+  for (int rb = 0; rb < NR; ++rb) {
+    const float m_use = (st.m[rb] == -INFINITY) ? 0.f : st.m[rb];
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      p[rb][j] = __builtin_amdgcn_exp2f(sc[j] - m_use);
+      p[rb][j] = __builtin_amdgcn_exp2f(sc[rb][j] - m_use);
       psum += p[rb][j];
     }
-    st.l[rb] = st.l[rb] * alpha + psum;
-    st.m[rb] = m_new;
-#pragma unroll
-    for (int i = 0; i < F::kBlocks; ++i) st.o[rb][i] *= alpha;
+    st.l[rb] += psum;
   }
 
   // ---------------- O^T += V_tile^T . P^T
@@ -230,16 +281,15 @@ __device__ __forceinline__ int out_dim(int sx, int grp, int j) {
 template <int D, int NR, bool BF16>
 constexpr bool pipelined() {
   using F = Frag<D, BF16>;
-  constexpr int q = NR * F::kQRegs * 4;
+  constexpr int q = QOperand<D, NR, BF16>::kInLds ? 0 : NR * F::kQRegs * 4;
   constexpr int o = NR * F::kBlocks * 4;
   constexpr int tile = F::kQRegs * 4 + 4 * F::kSets * F::kVWords;
-  return q + o + 2 * tile <= 224 && !(BF16 && D == 128 && NR == 3);
+  return q + o + 2 * tile <= 224 && o <= 96;
 }
 
 template <int D, int NR, bool BF16>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_splits,
-                                                              int keys_per_split, int n_chunks,
-                                                              int chunk_rows) {
+                                                              int n_chunks, int chunk_rows) {
   using F = Frag<D, BF16>;
   constexpr int kRows = 16 * NR;
   constexpr int kPitch = D + 4;  // LDS row pitch (floats): rows start 4 banks apart
@@ -262,9 +312,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   int n = a.seq_len[b];
   n = max(n, 0);
   n = min(n, a.limit);
-  const int kb = split * keys_per_split;
-  const int ke = min(kb + keys_per_split, n);
-  const int last = ke - 1;
+  const int last = n - 1;
 
   const int r16 = lane & 15;
   const int grp = lane >> 4;
@@ -272,17 +320,26 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   const char* kbase = static_cast<const char*>(a.k) + head_off;
   const char* vbase = static_cast<const char*>(a.v) + head_off;
 
-  // first tile of this wavefront: issued before anything else
-  constexpr int kStride = kWavesPerBlock * kTileKeys;
-  int t = kb + kTileKeys * wave;
+  // Tiles are dealt grid-stride: wavefront (split, wave) takes tiles (split*4 + wave) + k*(4*
+  // n_splits), so all workgroups sweep the cache together (the access pattern HBM streams best);
+  // the log-sum-exp merge does not care which keys a partial holds. The first tile is issued before
+  // anything else. Loads are clamped to row `last` and issued unconditionally once the wavefront has
+  // work (a prefetch past the end re-reads row `last` and is never used), so the compiler waits for
+  // exactly the older tile instead of draining every outstanding load. capacity <= 2^30 keeps every
+  // index below 2^31.
+  const int kStride = n_splits * kWavesPerBlock * kTileKeys;
+  int t = (split * kWavesPerBlock + wave) * kTileKeys;
   Tile<D, BF16> A, B;
-  if (t < ke) load_tile<D, BF16>(kbase, vbase, t, last, r16, grp, A);
+  if (t < n) load_tile<D, BF16>(kbase, vbase, t, last, r16, grp, A);
 
   // ---- query rows of this lane: row = row0 + rb*16 + r16 -> candidate jq, head hq
+  using QOp = QOperand<D, NR, BF16>;
+  __shared__ uint4 sm_q[QOp::kInLds ? NR * F::kQRegs * 64 : 1];
   int last_visible[NR];  // largest key index the row may attend
   bool row_ok[NR];
-  typedef typename std::conditional<BF16, bf16x8_t, f32x4_t>::type QVec;
-  QVec qf[NR][F::kQRegs];
+  QOp qf;
+  qf.lds = sm_q;
+  qf.lane = lane;
 #pragma unroll
   for (int rb = 0; rb < NR; ++rb) {
     const int row = row0 + rb * 16 + r16;
@@ -290,26 +347,22 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
     const int jq = row_ok[rb] ? row / G : 0;
     const int hq = h * G + (row_ok[rb] ? row % G : 0);
     last_visible[rb] = (a.mode == kModeVerify) ? (n - a.m + jq) : (n - 1);
+    if (QOp::kInLds && rb % kWavesPerBlock != wave) continue;  // LDS copy: one wave per row block
     const size_t qoff = ((size_t)(b * a.m + jq) * a.n_q_heads + hq) * D;
 #pragma unroll
     for (int ks = 0; ks < F::kQRegs; ++ks) {
-      if constexpr (BF16) {
-        // dims ks*32 + grp*8 .. +7 (the chunk the K operand holds)
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (row_ok[rb])
-          raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qoff +
-                                                ks * 32 + grp * 8);
-        qf[rb][ks] = __builtin_bit_cast(bf16x8_t, raw);
-      } else {
-        // dims ks*16 + grp*4 .. +3
-        float4 raw = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (row_ok[rb])
-          raw = *reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qoff + ks * 16 +
-                                                 grp * 4);
-        qf[rb][ks] = f32x4_t{raw.x, raw.y, raw.z, raw.w};
-      }
+      // bf16: dims ks*32 + grp*8 .. +7; fp32: dims ks*16 + grp*4 .. +3 (the chunk K holds)
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (row_ok[rb])
+        raw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + qoff * F::kEB +
+                                              (ks * 4 + grp) * 16);
+      if constexpr (QOp::kInLds)
+        sm_q[(rb * F::kQRegs + ks) * 64 + lane] = raw;
+      else
+        qf.reg[rb][ks] = __builtin_bit_cast(typename QOp::Vec, raw);
     }
   }
+  if constexpr (QOp::kInLds) __syncthreads();
 
   const float scale_log2 = a.sm_scale * kLog2e;
   RowState<D, NR, BF16> st;
@@ -323,24 +376,22 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
 
   if constexpr (pipelined<D, NR, BF16>()) {
     // software-pipelined tile loop: two register tiles, the next one always in flight
-    while (t < ke) {
-      int tn = t + kStride;
-      if (tn < ke) load_tile<D, BF16>(kbase, vbase, tn, last, r16, grp, B);
+    while (t < n) {
+      load_tile<D, BF16>(kbase, vbase, t + kStride, last, r16, grp, B);
       compute_tile<D, NR, BF16>(A, qf, t, last, last_visible, grp, scale_log2, st);
-      t = tn;
-      if (t >= ke) break;
-      tn = t + kStride;
-      if (tn < ke) load_tile<D, BF16>(kbase, vbase, tn, last, r16, grp, A);
+      t += kStride;
+      if (t >= n) break;
+      load_tile<D, BF16>(kbase, vbase, t + kStride, last, r16, grp, A);
       compute_tile<D, NR, BF16>(B, qf, t, last, last_visible, grp, scale_log2, st);
-      t = tn;
+      t += kStride;
     }
   } else {
     // one register tile: loads of tile t + stride start once tile t is consumed
     (void)B;
-    while (t < ke) {
+    while (t < n) {
       compute_tile<D, NR, BF16>(A, qf, t, last, last_visible, grp, scale_log2, st);
       t += kStride;
-      if (t < ke) load_tile<D, BF16>(kbase, vbase, t, last, r16, grp, A);
+      if (t < n) load_tile<D, BF16>(kbase, vbase, t, last, r16, grp, A);
     }
   }
 
@@ -527,10 +578,10 @@ hipError_t launch_split(const AttnArgs& a, const SplitPlan& p, hipStream_t strea
   constexpr int kMaxNr = BF16 ? (D == 256 ? 2 : 4) : (D == 64 ? 4 : (D == 128 ? 2 : 1));
   if (p.nr < 1 || p.nr > kMaxNr) return hipErrorInvalidValue;
   switch (p.nr) {
-    case 1: attn_split_kernel<D, 1, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.keys_per_split, p.n_chunks, p.chunk_rows); break;
-    case 2: if constexpr (kMaxNr >= 2) attn_split_kernel<D, 2, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.keys_per_split, p.n_chunks, p.chunk_rows); break;
-    case 3: if constexpr (kMaxNr >= 3) attn_split_kernel<D, 3, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.keys_per_split, p.n_chunks, p.chunk_rows); break;
-    default: if constexpr (kMaxNr >= 4) attn_split_kernel<D, 4, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.keys_per_split, p.n_chunks, p.chunk_rows); break;
+    case 1: attn_split_kernel<D, 1, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+    case 2: if constexpr (kMaxNr >= 2) attn_split_kernel<D, 2, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+    case 3: if constexpr (kMaxNr >= 3) attn_split_kernel<D, 3, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+    default: if constexpr (kMaxNr >= 4) attn_split_kernel<D, 4, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -551,7 +602,7 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
                    int max_seq_len, int dtype, SplitPlan* p) {
   if (batch < 1 || n_kv_heads < 1 || n_q_heads < n_kv_heads || n_q_heads % n_kv_heads) return false;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return false;
-  if (m < 1 || m > kMaxM || max_seq_len < 1) return false;
+  if (m < 1 || m > kMaxM || max_seq_len < 1 || max_seq_len > kMaxCapacity) return false;
   p->G = n_q_heads / n_kv_heads;
   p->rows = p->G * m;
   const int cap = rows_cap(dtype, head_dim);
@@ -560,12 +611,14 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
   p->nr = (p->chunk_rows + 15) / 16;
   const long long bhc = (long long)batch * n_kv_heads * p->n_chunks;
   const long long tiles_per_seq = ((long long)max_seq_len + kTileKeys - 1) / kTileKeys;
-  // at least one tile per wavefront, otherwise about kTargetBlocks workgroups in all
-  long long tps = (bhc * tiles_per_seq + kTargetBlocks - 1) / kTargetBlocks;
-  if (tps < kWavesPerBlock) tps = kWavesPerBlock;
-  if (tps > tiles_per_seq) tps = tiles_per_seq;
-  p->keys_per_split = (int)(tps * kTileKeys);
-  p->n_splits = (int)((max_seq_len + (long long)p->keys_per_split - 1) / p->keys_per_split);
+  // about kTargetBlocks workgroups in all, but at least one tile per wavefront
+  long long blocks = (bhc * tiles_per_seq + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > kTargetBlocks) blocks = kTargetBlocks;
+  long long per = (blocks + bhc - 1) / bhc;
+  const long long cap_per = (tiles_per_seq + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (per > cap_per) per = cap_per;
+  if (per < 1) per = 1;
+  p->n_splits = (int)per;
   p->ws_o_floats = (size_t)bhc * p->n_splits * 16 * p->nr * head_dim;
   p->ws_ml_floats = (size_t)bhc * p->n_splits * 16 * p->nr * 2;
   return true;

@@ -9,25 +9,28 @@
 
 namespace wmtp {
 
-// Work split of one attention call (split-K flash decoding). Every (sequence, KV head, row chunk)
-// is cut into n_splits key ranges of keys_per_split keys; one workgroup owns one key range and
-// leaves an un-normalised partial result (o, running max, running sum) in the workspace, which a
-// second kernel merges with the log-sum-exp rule. The plan depends only on the call's sizes.
+// Work split of one attention call (split-K flash decoding). The keys of every (sequence, KV head,
+// row chunk) are dealt in 16-key tiles over n_splits workgroups; each workgroup leaves one
+// un-normalised partial result (o, running max, running sum) in the workspace, which a second
+// kernel merges with the log-sum-exp rule. The plan depends only on the call's sizes.
 struct SplitPlan {
   int G;               // query heads per KV head
   int rows;            // G * m query rows per KV head
   int n_chunks;        // row chunks handled by separate wavefronts
   int chunk_rows;      // rows of a chunk (the last one may hold fewer)
   int nr;              // 16-row MFMA blocks per chunk: ceil(chunk_rows / 16)
-  int keys_per_split;  // multiple of kTileKeys
-  int n_splits;        // key ranges per (sequence, KV head, chunk)
+  int n_splits;        // workgroups (partials) per (sequence, KV head, chunk)
   size_t ws_o_floats;  // partial outputs: [bhc][n_splits][16*nr][head_dim]
   size_t ws_ml_floats; // running max and sum: [bhc][n_splits][16*nr][2]
 };
 
 constexpr int kTileKeys = 16;       // keys per MFMA tile
 constexpr int kWavesPerBlock = 4;   // wavefronts per workgroup (interleaved tiles of one range)
-constexpr int kTargetBlocks = 512;  // about two workgroups per CU (256 CUs)
+#ifndef WMTP_TARGET_BLOCKS
+#define WMTP_TARGET_BLOCKS 512
+#endif
+constexpr int kTargetBlocks = WMTP_TARGET_BLOCKS;  // workgroups per call (256 CUs)
+constexpr int kMaxCapacity = 1 << 30;              // keeps key indices below 2^31
 constexpr int kMaxM = 16;           // verify candidates per call
 
 // Plan for a cache of `dtype`; false when no attention call accepts these sizes.

@@ -70,7 +70,8 @@ typedef enum wmtp_status {
 typedef enum wmtp_dtype { WMTP_F32 = 0, WMTP_BF16 = 1 } wmtp_dtype;
 
 /* A KV cache of `batch` sequences: a compact ring buffer (window >= 1, capacity = sink + window) or
- * a contiguous cache (window = 0, sink = capacity). head_dim must be 64, 128 or 256. */
+ * a contiguous cache (window = 0, sink = capacity). head_dim must be 64, 128 or 256;
+ * 1 <= capacity <= 2^30 (larger capacities return WMTP_ERR_CAPACITY). */
 typedef struct wmtp_kv {
   void* k;          /* device [batch][n_kv_heads][capacity][head_dim] */
   void* v;          /* device [batch][n_kv_heads][capacity][head_dim] */

@@ -469,6 +469,266 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Cooperative-tile kernel. The four wavefronts of a workgroup consume the SAME 16-key tile, which
+// the whole workgroup stages through LDS: every thread issues fully coalesced 16-byte loads for its
+// share of the tile (K and V rows are contiguous in HBM), keeps kPrefetch tiles of them in flight
+// in registers, and writes the oldest one into a double-buffered LDS stage (16-byte chunks XOR-
+// swizzled by key so the operand reads below are bank-conflict free). One barrier per tile.
+// The wavefronts split the work of a tile either by query-row block (NB = 4 blocks of 16 rows, the
+// verify shape) or by output dimensions (NB = 1: each wavefront owns D/4 dims of all 16 rows and
+// recomputes the 16x16 score tile, which is cheap on the matrix cores). Each wavefront writes its
+// own part of the workgroup's partial; no cross-wavefront merge is needed.
+template <int D, int NB, bool BF16>
+struct Coop {
+  static constexpr int kEB = BF16 ? 2 : 4;
+  static constexpr int kRowBytes = D * kEB;
+  static constexpr int kChunks = kRowBytes / 16;             // 16-byte chunks per key row
+  static constexpr int kSwz = (kChunks < 16 ? kChunks : 16) - 1;
+  static constexpr int kSplitD = kWavesPerBlock / NB;         // wavefronts sharing a row block
+  static constexpr int kDw = D / kSplitD;                     // output dims per wavefront
+  static constexpr int kDpl = kDw / 16;                       // V dims per lane (= output blocks)
+  static constexpr int kQRegs = BF16 ? D / 32 : D / 16;       // 16-byte Q/K pieces per lane
+  static constexpr int kTileBytes = 16 * kRowBytes;           // K (or V) bytes of one tile
+  static constexpr int kLoads = 2 * 16 * kChunks / kThreads;  // 16-byte loads per thread per tile
+#ifdef WMTP_COOP_PREFETCH
+  static constexpr int kPrefetch = WMTP_COOP_PREFETCH;
+#else
+  static constexpr int kPrefetch = kLoads >= 8 ? 2 : (kLoads >= 4 ? 4 : 6);
+#endif
+  static_assert(kLoads >= 1 && 2 * 16 * kChunks % kThreads == 0, "tile must split evenly");
+  static_assert(kDpl >= (BF16 ? 2 : 1), "each lane needs a pair of bf16 dims");
+};
+
+template <int D, int NB, bool BF16>
+__device__ __forceinline__ int coop_slot(int key, int chunk) {
+  using C = Coop<D, NB, BF16>;
+  return key * C::kRowBytes + ((chunk ^ (key & C::kSwz)) << 4);
+}
+
+template <int D, int NB, bool BF16>
+__global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int n_splits,
+                                                                 int n_chunks, int chunk_rows) {
+  using C = Coop<D, NB, BF16>;
+  typedef typename std::conditional<BF16, bf16x8_t, f32x4_t>::type QVec;
+  __shared__ __attribute__((aligned(16))) char sm_tile[2][2 * C::kTileBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rb = wave / C::kSplitD;  // row block of this wavefront
+  const int d0 = (wave % C::kSplitD) * C::kDw;
+  const int split = blockIdx.x;
+  const int bhc = blockIdx.y;
+  const int chunk = bhc % n_chunks;
+  const int bh = bhc / n_chunks;
+  const int h = bh % a.n_kv_heads;
+  const int b = bh / a.n_kv_heads;
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int rows = G * a.m;
+  const int row_end = min(rows, chunk * chunk_rows + chunk_rows);
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+
+  int n = a.seq_len[b];
+  n = max(n, 0);
+  n = min(n, a.limit);
+  const int last = n - 1;
+  const int tiles = (n + kTileKeys - 1) / kTileKeys;
+  const int my_tiles = split < tiles ? (tiles - split + n_splits - 1) / n_splits : 0;
+
+  const size_t head_off = (size_t)(b * a.n_kv_heads + h) * (size_t)a.capacity * C::kRowBytes;
+  const char* kbase = static_cast<const char*>(a.k) + head_off;
+  const char* vbase = static_cast<const char*>(a.v) + head_off;
+
+  // staging: load l of this thread is chunk q = tid + kThreads*l of the tile (K chunks first)
+  uint4 stg[C::kPrefetch][C::kLoads];
+  auto tile_start = [&](int i) {  // first key of the workgroup's i-th tile, clamped into range
+    const int tl = split + i * n_splits;
+    return (tl < tiles ? tl : tiles - 1) * kTileKeys;
+  };
+  auto load_stage = [&](uint4(&dst)[C::kLoads], int t0) {
+#pragma unroll
+    for (int l = 0; l < C::kLoads; ++l) {
+      const int q = tid + kThreads * l;
+      const int tensor = q / (16 * C::kChunks);
+      const int key = (q / C::kChunks) % 16;
+      const int c = q % C::kChunks;
+      const int kg = min(t0 + key, last);
+      dst[l] = stream_load16((tensor ? vbase : kbase) + (size_t)kg * C::kRowBytes + c * 16);
+    }
+  };
+  auto store_stage = [&](const uint4(&src)[C::kLoads], int buf) {
+#pragma unroll
+    for (int l = 0; l < C::kLoads; ++l) {
+      const int q = tid + kThreads * l;
+      const int tensor = q / (16 * C::kChunks);
+      const int key = (q / C::kChunks) % 16;
+      const int c = q % C::kChunks;
+      *reinterpret_cast<uint4*>(&sm_tile[buf][tensor * C::kTileBytes +
+                                              coop_slot<D, NB, BF16>(key, c)]) = src[l];
+    }
+  };
+
+  if (my_tiles > 0) {
+#pragma unroll
+    for (int s = 0; s < C::kPrefetch; ++s) load_stage(stg[s], tile_start(s));
+  }
+
+  // query operand of this wavefront's row block
+  const int row = chunk * chunk_rows + rb * 16 + r16;
+  const bool row_ok = row < row_end;
+  const int jq = row_ok ? row / G : 0;
+  const int hq = h * G + (row_ok ? row % G : 0);
+  const int last_visible = (a.mode == kModeVerify) ? (n - a.m + jq) : (n - 1);
+  QVec qf[C::kQRegs];
+  {
+    const size_t qoff = ((size_t)(b * a.m + jq) * a.n_q_heads + hq) * D;
+#pragma unroll
+    for (int ks = 0; ks < C::kQRegs; ++ks) {
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (row_ok)
+        raw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + qoff * C::kEB +
+                                              (ks * 4 + grp) * 16);
+      qf[ks] = __builtin_bit_cast(QVec, raw);
+    }
+  }
+
+  const float scale_log2 = a.sm_scale * kLog2e;
+  float m_ref = -INFINITY;  // reference max (log2 units), shared by the row's four lanes
+  float l_lane = 0.f;       // this lane's share of the running sum
+  f32x4_t o[C::kDpl];
+#pragma unroll
+  for (int e = 0; e < C::kDpl; ++e) o[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int base = 0; base < my_tiles; base += C::kPrefetch) {
+#pragma unroll
+    for (int s = 0; s < C::kPrefetch; ++s) {
+      const int i = base + s;
+      if (i >= my_tiles) break;  // workgroup-uniform
+      const int buf = i & 1;
+      store_stage(stg[s], buf);
+      load_stage(stg[s], tile_start(i + C::kPrefetch));
+      __syncthreads();  // tile i visible; every wavefront is done with tile i-1's buffer
+      const int t0 = tile_start(i);
+      const char* kt = sm_tile[buf];
+      const char* vt = sm_tile[buf] + C::kTileBytes;
+
+      // ---- S^T (16 keys x 16 rows) for this row block
+      f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < C::kQRegs; ++ks) {
+        const uint4 kv =
+            *reinterpret_cast<const uint4*>(kt + coop_slot<D, NB, BF16>(r16, ks * 4 + grp));
+        if constexpr (BF16) {
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qf[ks],
+                                                         sacc, 0, 0, 0);
+        } else {
+          const float4 kf = __builtin_bit_cast(float4, kv);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.x, qf[ks][0], sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.y, qf[ks][1], sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.z, qf[ks][2], sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.w, qf[ks][3], sacc, 0, 0, 0);
+        }
+      }
+
+      // ---- softmax with a lazily moved reference max (see compute_tile)
+      const int vis = min(last, last_visible);
+      float sc[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = t0 + 4 * grp + j;
+        sc[j] = (key <= vis) ? sacc[j] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sc[j]);
+      }
+      mx = xgroup_max(mx);
+      const bool moved = mx > m_ref + kRescaleLog2;
+      if (__ballot(moved)) {
+        const float alpha = moved ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;
+        l_lane *= alpha;
+#pragma unroll
+        for (int e = 0; e < C::kDpl; ++e) o[e] *= alpha;
+        m_ref = moved ? mx : m_ref;
+      }
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(sc[j] - m_use);
+        l_lane += p[j];
+      }
+
+      // ---- O^T (this wavefront's dims) += V^T . P^T; lane r16 owns dims d0 + kDpl*r16 + e
+      constexpr int kVBytes = C::kDpl * C::kEB;  // bytes per key per lane
+      constexpr int kVWords = kVBytes / 4;
+      uint32_t vw[4][kVWords];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int key = 4 * grp + t;
+        const int bo = (d0 + C::kDpl * r16) * C::kEB;  // byte offset in the key row
+#pragma unroll
+        for (int w = 0; w < kVWords; w += (kVWords >= 4 ? 4 : kVWords)) {
+          const int byte = bo + 4 * w;
+          const char* src = vt + coop_slot<D, NB, BF16>(key, byte >> 4) + (byte & 15);
+          if constexpr (kVWords >= 4) {
+            const uint4 x = *reinterpret_cast<const uint4*>(src);
+            vw[t][w] = x.x; vw[t][w + 1] = x.y; vw[t][w + 2] = x.z; vw[t][w + 3] = x.w;
+          } else if constexpr (kVWords == 2) {
+            const uint2 x = *reinterpret_cast<const uint2*>(src);
+            vw[t][0] = x.x; vw[t][1] = x.y;
+          } else {
+            vw[t][0] = *reinterpret_cast<const uint32_t*>(src);
+          }
+        }
+      }
+      if constexpr (BF16) {
+        const bf16x4_t pb = __builtin_convertvector(f32x4_t{p[0], p[1], p[2], p[3]}, bf16x4_t);
+        const s16x4_t pop = __builtin_bit_cast(s16x4_t, pb);
+#pragma unroll
+        for (int w = 0; w < kVWords; ++w)
+#pragma unroll
+          for (int hi = 0; hi < 2; ++hi) {
+            const uint32_t k01 = pack_halves(vw[0][w], vw[1][w], hi);
+            const uint32_t k23 = pack_halves(vw[2][w], vw[3][w], hi);
+            const s16x4_t vop = __builtin_bit_cast(s16x4_t, make_uint2(k01, k23));
+            o[2 * w + hi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, o[2 * w + hi], 0, 0, 0);
+          }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < C::kDpl; ++e)
+            o[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, vw[u][e]), p[u],
+                                                        o[e], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- this wavefront's part of the workgroup's partial
+  const float l_row = xgroup_sum(l_lane);
+  if (!row_ok) return;
+  const size_t part = (size_t)bhc * n_splits + split;
+  constexpr int kRows = 16 * NB;
+  const int rloc = rb * 16 + r16;
+  float* dst = a.ws_o + (part * kRows + rloc) * D + d0;
+  // lane (r16, grp) holds O^T rows 4*grp + j of block e: dim d0 + kDpl*(4*grp + j) + e
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float* d = dst + C::kDpl * (4 * grp + j);
+    if constexpr (C::kDpl >= 4) {
+#pragma unroll
+      for (int e = 0; e < C::kDpl; e += 4)
+        *reinterpret_cast<float4*>(d + e) = make_float4(o[e][j], o[e + 1][j], o[e + 2][j], o[e + 3][j]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < C::kDpl; ++e) d[e] = o[e][j];
+    }
+  }
+  if (d0 == 0 && grp == 0)
+    *reinterpret_cast<float2*>(a.ws_ml + (part * kRows + rloc) * 2) = make_float2(m_ref, l_row);
+}
+
 // One workgroup per (output row, 64 dims). 16 threads cover the 64 dims as float4 columns; 16
 // lanes of splits stride over the partials with independent loads, then combine through LDS.
 template <int D>
@@ -590,6 +850,23 @@ hipError_t launch_split(const AttnArgs& a, const SplitPlan& p, hipStream_t strea
   return hipGetLastError();
 }
 
+template <int D, bool BF16>
+hipError_t launch_coop(const AttnArgs& a, const SplitPlan& p, hipStream_t stream) {
+  dim3 grid(p.n_splits, a.batch * a.n_kv_heads * p.n_chunks);
+  dim3 block(kThreads);
+  switch (p.nr) {
+    case 1: if constexpr (!(BF16 && D == 64)) attn_coop_kernel<D, 1, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+    case 2: attn_coop_kernel<D, 2, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+    case 4: if constexpr (BF16 || D != 256) attn_coop_kernel<D, 4, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  merge_kernel<D><<<dim3(a.batch * a.m * a.n_q_heads, D / 64), dim3(256), 0, stream>>>(
+      a, p.n_splits, p.n_chunks, p.chunk_rows, p.nr);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // Largest row chunk whose Q operand and O accumulators fit the register file beside the K/V tiles.
@@ -605,15 +882,27 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
   if (m < 1 || m > kMaxM || max_seq_len < 1 || max_seq_len > kMaxCapacity) return false;
   p->G = n_q_heads / n_kv_heads;
   p->rows = p->G * m;
-  const int cap = rows_cap(dtype, head_dim);
+  // key-split kernel for a single row block (draft steps), cooperative tiles for several (verify);
+  // each with the workgroup count measured best for it on MI355X
+  p->coop = kAllowCoop && p->rows > 16;
+  const int target_blocks = p->coop ? kTargetBlocksCoop : kTargetBlocksSplit;
+  // fp32 with head_dim 256 keeps at most two row blocks per workgroup (register budget)
+  const int coop_cap = (dtype == WMTP_F32 && head_dim == 256) ? 32 : kWavesPerBlock * 16;
+  const int cap = p->coop ? coop_cap : rows_cap(dtype, head_dim);
   p->chunk_rows = p->rows < cap ? p->rows : cap;
   p->n_chunks = (p->rows + p->chunk_rows - 1) / p->chunk_rows;
   p->nr = (p->chunk_rows + 15) / 16;
+  if (p->coop) {
+    // row blocks per workgroup: 1, 2 or 4 (the wavefronts split the rest by dims); a bf16 lane
+    // needs at least two dims, so head_dim 64 keeps two row blocks
+    if (p->nr == 3) p->nr = 4;
+    if (dtype == WMTP_BF16 && head_dim == 64 && p->nr < 2) p->nr = 2;
+  }
   const long long bhc = (long long)batch * n_kv_heads * p->n_chunks;
   const long long tiles_per_seq = ((long long)max_seq_len + kTileKeys - 1) / kTileKeys;
-  // about kTargetBlocks workgroups in all, but at least one tile per wavefront
+  // about target_blocks workgroups in all, but at least one tile per wavefront
   long long blocks = (bhc * tiles_per_seq + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks > kTargetBlocks) blocks = kTargetBlocks;
+  if (blocks > target_blocks) blocks = target_blocks;
   long long per = (blocks + bhc - 1) / bhc;
   const long long cap_per = (tiles_per_seq + kWavesPerBlock - 1) / kWavesPerBlock;
   if (per > cap_per) per = cap_per;
@@ -626,6 +915,14 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
 
 hipError_t launch_attention(const AttnArgs& a, const SplitPlan& p, int dtype, hipStream_t stream) {
   const bool bf16 = dtype == WMTP_BF16;
+  if (p.coop) {
+    switch (a.head_dim) {
+      case 64: return bf16 ? launch_coop<64, true>(a, p, stream) : launch_coop<64, false>(a, p, stream);
+      case 128: return bf16 ? launch_coop<128, true>(a, p, stream) : launch_coop<128, false>(a, p, stream);
+      case 256: return bf16 ? launch_coop<256, true>(a, p, stream) : launch_coop<256, false>(a, p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.head_dim) {
     case 64: return bf16 ? launch_split<64, true>(a, p, stream) : launch_split<64, false>(a, p, stream);
     case 128: return bf16 ? launch_split<128, true>(a, p, stream) : launch_split<128, false>(a, p, stream);

@@ -18,7 +18,8 @@ struct SplitPlan {
   int rows;            // G * m query rows per KV head
   int n_chunks;        // row chunks handled by separate wavefronts
   int chunk_rows;      // rows of a chunk (the last one may hold fewer)
-  int nr;              // 16-row MFMA blocks per chunk: ceil(chunk_rows / 16)
+  bool coop;           // cooperative-tile kernel (else the key-split kernel)
+  int nr;              // 16-row MFMA blocks per chunk
   int n_splits;        // workgroups (partials) per (sequence, KV head, chunk)
   size_t ws_o_floats;  // partial outputs: [bhc][n_splits][16*nr][head_dim]
   size_t ws_ml_floats; // running max and sum: [bhc][n_splits][16*nr][2]
@@ -26,11 +27,20 @@ struct SplitPlan {
 
 constexpr int kTileKeys = 16;       // keys per MFMA tile
 constexpr int kWavesPerBlock = 4;   // wavefronts per workgroup (interleaved tiles of one range)
-#ifndef WMTP_TARGET_BLOCKS
-#define WMTP_TARGET_BLOCKS 512
+// workgroups per call (256 CUs), measured best for each kernel on MI355X at L = 1M
+#ifndef WMTP_TARGET_BLOCKS_SPLIT
+#define WMTP_TARGET_BLOCKS_SPLIT 256
 #endif
-constexpr int kTargetBlocks = WMTP_TARGET_BLOCKS;  // workgroups per call (256 CUs)
-constexpr int kMaxCapacity = 1 << 30;              // keeps key indices below 2^31
+#ifndef WMTP_TARGET_BLOCKS_COOP
+#define WMTP_TARGET_BLOCKS_COOP 768
+#endif
+#ifndef WMTP_ALLOW_COOP
+#define WMTP_ALLOW_COOP 1
+#endif
+constexpr int kTargetBlocksSplit = WMTP_TARGET_BLOCKS_SPLIT;
+constexpr int kTargetBlocksCoop = WMTP_TARGET_BLOCKS_COOP;
+constexpr bool kAllowCoop = WMTP_ALLOW_COOP != 0;
+constexpr int kMaxCapacity = 1 << 30;  // keeps key indices below 2^31
 constexpr int kMaxM = 16;           // verify candidates per call
 
 // Plan for a cache of `dtype`; false when no attention call accepts these sizes.

@@ -36,7 +36,51 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (reference for "
+                         "scaling the HBM byte counters of a profiler) and exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 3}), flush=True)
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_decode_step_L1M.txt")
+
+
+def attn_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("attn.hip", "wmtp_internal.h"):
+        with open(os.path.join(ROOT, "draft_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch (profiler FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading)
+    from the committed summary, or None when the attention source changed since it was taken."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            fields = dict(l.split(": ", 1) for l in fh.read().splitlines() if ": " in l)
+    except OSError:
+        return None
+    if fields.get("attn_source_sha256", "").strip() != attn_source_hash():
+        return None
+    v = fields.get(f"traffic_bytes_per_launch.{kind}")
+    return None if v is None else int(float(v))
 
 
 def fill_sequence(dst, seed, tensor_id, b, p0, p1, dtype, device, chunk=1 << 17):
@@ -51,6 +95,9 @@ def fill_sequence(dst, seed, tensor_id, b, p0, p1, dtype, device, chunk=1 << 17)
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the hot path "
               "has no multi-GPU form", file=sys.stderr)
@@ -224,7 +271,9 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(gbs(b_full, mean_us["full_attn"]) / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("full"),
+            "traffic_unit": "bytes per launch (split-K kernel; null if the kernel changed since "
+                            "the counters in profiles/ were taken)",
         },
         "cpu_baseline": None,
     }

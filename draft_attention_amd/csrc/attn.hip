@@ -330,7 +330,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   const int kStride = n_splits * kWavesPerBlock * kTileKeys;
   int t = (split * kWavesPerBlock + wave) * kTileKeys;
   Tile<D, BF16> A, B;
-  if (t < n) load_tile<D, BF16>(kbase, vbase, t, last, r16, grp, A);
+  // The first tile is requested against the host-side bound (a.limit >= 1, so row limit-1 is
+  // always a valid address) without waiting for seq_len: the loads overlap the seq_len read, and
+  // seq_len only masks. Later tiles clamp to the last real key.
+  if (t < a.limit) load_tile<D, BF16>(kbase, vbase, t, min(a.limit - 1, t + kTileKeys - 1), r16, grp, A);
 
   // ---- query rows of this lane: row = row0 + rb*16 + r16 -> candidate jq, head hq
   using QOp = QOperand<D, NR, BF16>;
@@ -344,18 +347,18 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   for (int rb = 0; rb < NR; ++rb) {
     const int row = row0 + rb * 16 + r16;
     row_ok[rb] = row < row_end;
-    const int jq = row_ok[rb] ? row / G : 0;
-    const int hq = h * G + (row_ok[rb] ? row % G : 0);
+    // padding rows load the last real row (never written out; no select, so no early wait)
+    const int row_q = row_ok[rb] ? row : row_end - 1;
+    const int jq = row_q / G;
+    const int hq = h * G + row_q % G;
     last_visible[rb] = (a.mode == kModeVerify) ? (n - a.m + jq) : (n - 1);
     if (QOp::kInLds && rb % kWavesPerBlock != wave) continue;  // LDS copy: one wave per row block
     const size_t qoff = ((size_t)(b * a.m + jq) * a.n_q_heads + hq) * D;
 #pragma unroll
     for (int ks = 0; ks < F::kQRegs; ++ks) {
       // bf16: dims ks*32 + grp*8 .. +7; fp32: dims ks*16 + grp*4 .. +3 (the chunk K holds)
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (row_ok[rb])
-        raw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + qoff * F::kEB +
-                                              (ks * 4 + grp) * 16);
+      const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
+                                                        qoff * F::kEB + (ks * 4 + grp) * 16);
       if constexpr (QOp::kInLds)
         sm_q[(rb * F::kQRegs + ks) * 64 + lane] = raw;
       else
@@ -490,13 +493,19 @@ struct Coop {
   static constexpr int kDpl = kDw / 16;                       // V dims per lane (= output blocks)
   static constexpr int kQRegs = BF16 ? D / 32 : D / 16;       // 16-byte Q/K pieces per lane
   static constexpr int kTileBytes = 16 * kRowBytes;           // K (or V) bytes of one tile
-  static constexpr int kLoads = 2 * 16 * kChunks / kThreads;  // 16-byte loads per thread per tile
+#ifdef WMTP_COOP_TPS
+  static constexpr int kTps = WMTP_COOP_TPS;                   // tiles per LDS stage (per barrier)
+#else
+  static constexpr int kTps = 1;
+#endif
+  static constexpr int kStageBytes = kTps * 2 * kTileBytes;   // K and V of the stage's tiles
+  static constexpr int kLoads = kStageBytes / 16 / kThreads;  // 16-byte loads per thread per stage
 #ifdef WMTP_COOP_PREFETCH
-  static constexpr int kPrefetch = WMTP_COOP_PREFETCH;
+  static constexpr int kPrefetch = WMTP_COOP_PREFETCH;       // stages in flight
 #else
   static constexpr int kPrefetch = kLoads >= 8 ? 2 : (kLoads >= 4 ? 4 : 6);
 #endif
-  static_assert(kLoads >= 1 && 2 * 16 * kChunks % kThreads == 0, "tile must split evenly");
+  static_assert(kLoads >= 1 && kStageBytes % (16 * kThreads) == 0, "stage must split evenly");
   static_assert(kDpl >= (BF16 ? 2 : 1), "each lane needs a pair of bf16 dims");
 };
 
@@ -511,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int 
                                                                  int n_chunks, int chunk_rows) {
   using C = Coop<D, NB, BF16>;
   typedef typename std::conditional<BF16, bf16x8_t, f32x4_t>::type QVec;
-  __shared__ __attribute__((aligned(16))) char sm_tile[2][2 * C::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char sm_tile[2][C::kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -536,25 +545,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int 
   const int last = n - 1;
   const int tiles = (n + kTileKeys - 1) / kTileKeys;
   const int my_tiles = split < tiles ? (tiles - split + n_splits - 1) / n_splits : 0;
+  const int my_stages = (my_tiles + C::kTps - 1) / C::kTps;
 
   const size_t head_off = (size_t)(b * a.n_kv_heads + h) * (size_t)a.capacity * C::kRowBytes;
   const char* kbase = static_cast<const char*>(a.k) + head_off;
   const char* vbase = static_cast<const char*>(a.v) + head_off;
 
-  // staging: load l of this thread is chunk q = tid + kThreads*l of the tile (K chunks first)
+  // staging: load l of this thread is chunk q = tid + kThreads*l of the stage: tile q / (32*kChunks),
+  // then K chunks before V chunks
   uint4 stg[C::kPrefetch][C::kLoads];
+  // Addresses only depend on the host-side bound a.limit (>= 1), so the first tiles are requested
+  // without waiting for seq_len; seq_len only masks (a tile past it is computed fully masked).
+  const int tiles_lim = (a.limit + kTileKeys - 1) / kTileKeys;
+  const int last_lim = a.limit - 1;
   auto tile_start = [&](int i) {  // first key of the workgroup's i-th tile, clamped into range
     const int tl = split + i * n_splits;
-    return (tl < tiles ? tl : tiles - 1) * kTileKeys;
+    return (tl < tiles_lim ? tl : tiles_lim - 1) * kTileKeys;
   };
-  auto load_stage = [&](uint4(&dst)[C::kLoads], int t0) {
+  auto load_stage = [&](uint4(&dst)[C::kLoads], int stage) {
 #pragma unroll
     for (int l = 0; l < C::kLoads; ++l) {
       const int q = tid + kThreads * l;
-      const int tensor = q / (16 * C::kChunks);
+      const int u = q / (32 * C::kChunks);  // tile of the stage
+      const int tensor = (q / (16 * C::kChunks)) & 1;
       const int key = (q / C::kChunks) % 16;
       const int c = q % C::kChunks;
-      const int kg = min(t0 + key, last);
+      const int kg = min(tile_start(stage * C::kTps + u) + key, last_lim);
       dst[l] = stream_load16((tensor ? vbase : kbase) + (size_t)kg * C::kRowBytes + c * 16);
     }
   };
@@ -562,36 +578,39 @@ __global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int 
 #pragma unroll
     for (int l = 0; l < C::kLoads; ++l) {
       const int q = tid + kThreads * l;
-      const int tensor = q / (16 * C::kChunks);
+      const int u = q / (32 * C::kChunks);
+      const int tensor = (q / (16 * C::kChunks)) & 1;
       const int key = (q / C::kChunks) % 16;
       const int c = q % C::kChunks;
-      *reinterpret_cast<uint4*>(&sm_tile[buf][tensor * C::kTileBytes +
+      *reinterpret_cast<uint4*>(&sm_tile[buf][(2 * u + tensor) * C::kTileBytes +
                                               coop_slot<D, NB, BF16>(key, c)]) = src[l];
     }
   };
 
-  if (my_tiles > 0) {
-#pragma unroll
-    for (int s = 0; s < C::kPrefetch; ++s) load_stage(stg[s], tile_start(s));
-  }
-
-  // query operand of this wavefront's row block
+  // query operand of this wavefront's row block. Loaded before the tile prefetch so that the
+  // loads outstanding at the top of the tile loop are the same on entry and on the back edge
+  // (otherwise the compiler drains every load there, once per round of kPrefetch tiles).
+  // A padding row (past the last query row) loads the last real row instead of zeros: its
+  // results are never written, and an unconditional load needs no wait before the prefetch.
   const int row = chunk * chunk_rows + rb * 16 + r16;
   const bool row_ok = row < row_end;
-  const int jq = row_ok ? row / G : 0;
-  const int hq = h * G + (row_ok ? row % G : 0);
+  const int row_q = row_ok ? row : row_end - 1;
+  const int jq = row_q / G;
+  const int hq = h * G + row_q % G;
   const int last_visible = (a.mode == kModeVerify) ? (n - a.m + jq) : (n - 1);
   QVec qf[C::kQRegs];
   {
     const size_t qoff = ((size_t)(b * a.m + jq) * a.n_q_heads + hq) * D;
 #pragma unroll
-    for (int ks = 0; ks < C::kQRegs; ++ks) {
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (row_ok)
-        raw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + qoff * C::kEB +
-                                              (ks * 4 + grp) * 16);
-      qf[ks] = __builtin_bit_cast(QVec, raw);
-    }
+    for (int ks = 0; ks < C::kQRegs; ++ks)
+      qf[ks] = __builtin_bit_cast(
+          QVec, *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + qoff * C::kEB +
+                                                (ks * 4 + grp) * 16));
+  }
+
+  if (split < tiles_lim) {
+#pragma unroll
+    for (int s = 0; s < C::kPrefetch; ++s) load_stage(stg[s], s);
   }
 
   const float scale_log2 = a.sm_scale * kLog2e;
@@ -601,18 +620,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int 
 #pragma unroll
   for (int e = 0; e < C::kDpl; ++e) o[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int base = 0; base < my_tiles; base += C::kPrefetch) {
+  // Rounds of exactly kPrefetch tiles with no early exit: tiles past the workgroup's share are
+  // computed fully masked. The straight-line round lets the compiler wait for exactly the oldest
+  // staged tile (an early exit inside the round makes it drain every load at the round start).
+  for (int base = 0; base < my_stages; base += C::kPrefetch) {
 #pragma unroll
     for (int s = 0; s < C::kPrefetch; ++s) {
-      const int i = base + s;
-      if (i >= my_tiles) break;  // workgroup-uniform
-      const int buf = i & 1;
+      const int st = base + s;
+      const int buf = st & 1;
       store_stage(stg[s], buf);
-      load_stage(stg[s], tile_start(i + C::kPrefetch));
-      __syncthreads();  // tile i visible; every wavefront is done with tile i-1's buffer
+      load_stage(stg[s], st + C::kPrefetch);
+      __syncthreads();  // stage st visible; every wavefront is done with stage st-1's buffer
+#pragma unroll
+      for (int u = 0; u < C::kTps; ++u) {
+      const int i = st * C::kTps + u;
+      const bool live = i < my_tiles;  // workgroup-uniform
       const int t0 = tile_start(i);
-      const char* kt = sm_tile[buf];
-      const char* vt = sm_tile[buf] + C::kTileBytes;
+      const char* kt = sm_tile[buf] + 2 * u * C::kTileBytes;
+      const char* vt = kt + C::kTileBytes;
 
       // ---- S^T (16 keys x 16 rows) for this row block
       f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -633,7 +658,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int 
       }
 
       // ---- softmax with a lazily moved reference max (see compute_tile)
-      const int vis = min(last, last_visible);
+      const int vis = live ? min(last, last_visible) : -1;
       float sc[4];
       float mx = -INFINITY;
 #pragma unroll
@@ -702,6 +727,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int 
             o[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, vw[u][e]), p[u],
                                                         o[e], 0, 0, 0);
       }
+      }
     }
   }
 
@@ -730,12 +756,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int 
 }
 
 // One workgroup per (output row, 64 dims). 16 threads cover the 64 dims as float4 columns; 16
-// lanes of splits stride over the partials with independent loads, then combine through LDS.
+// lanes of splits stride over the partials in one online pass (each lane keeps its own running max
+// and rescales), with all loads of an unrolled batch independent; the lanes then combine through
+// LDS with the same rescaling rule.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, int n_chunks,
                                                     int chunk_rows, int nr) {
   constexpr int kCols = 16;
   constexpr int kSplitLanes = 256 / kCols;
+  constexpr int kBatch = 8;
   __shared__ float red_m[256];
   __shared__ float4 red_o[256];
   __shared__ float red_l[256];
@@ -754,65 +783,60 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, in
   const size_t base = ((size_t)(b * a.n_kv_heads + h) * n_chunks + chunk) * n_splits;
   const int rows16 = 16 * nr;
   const int tid = threadIdx.x;
+  const int col = tid % kCols;
+  const int sl = tid / kCols;
   auto ml_at = [&](int s) {
     return *reinterpret_cast<const float2*>(a.ws_ml + ((base + s) * rows16 + rloc) * 2);
   };
-  auto o_at = [&](int s, int col) {
+  auto o_at = [&](int s) {
     return *reinterpret_cast<const float4*>(a.ws_o + ((base + s) * rows16 + rloc) * D + dim0 +
                                             col * 4);
   };
 
-  // pass 1: maximum of the running maxima of non-empty partials
-  float M = -INFINITY;
-  for (int s = tid; s < n_splits; s += 256) {
-    const float2 ml = ml_at(s);
-    if (ml.y > 0.f) M = fmaxf(M, ml.x);
-  }
-  red_m[tid] = M;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red_m[tid] = fmaxf(red_m[tid], red_m[tid + off]);
-    __syncthreads();
-  }
-  M = red_m[0];
-
-  // pass 2: rescaled sums, four partials in flight per thread
-  const int col = tid % kCols;
-  const int sl = tid / kCols;
+  // running state of this lane: sum_s 2^(m_s - M) (o_s, l_s) over the partials seen so far
+  float M = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float L = 0.f;
-  int s = sl;
-  for (; s + 3 * kSplitLanes < n_splits; s += 4 * kSplitLanes) {
-    float2 ml[4];
-    float4 x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ml[i] = ml_at(s + i * kSplitLanes);
-      x[i] = o_at(s + i * kSplitLanes, col);
+  auto absorb = [&](float2 ml, float4 x) {
+    if (!(ml.y > 0.f)) return;  // empty partial
+    if (ml.x > M) {
+      const float c = __builtin_amdgcn_exp2f(M - ml.x);  // 0 while M is -inf
+      L *= c; acc.x *= c; acc.y *= c; acc.z *= c; acc.w *= c;
+      M = ml.x;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float w = ml[i].y > 0.f ? __builtin_amdgcn_exp2f(ml[i].x - M) : 0.f;
-      L += w * ml[i].y;
-      acc.x += w * x[i].x; acc.y += w * x[i].y; acc.z += w * x[i].z; acc.w += w * x[i].w;
-    }
-  }
-  for (; s < n_splits; s += kSplitLanes) {
-    const float2 ml = ml_at(s);
-    const float4 x = o_at(s, col);
-    const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - M) : 0.f;
+    const float w = __builtin_amdgcn_exp2f(ml.x - M);
     L += w * ml.y;
     acc.x += w * x.x; acc.y += w * x.y; acc.z += w * x.z; acc.w += w * x.w;
+  };
+  int s = sl;
+  for (; s + (kBatch - 1) * kSplitLanes < n_splits; s += kBatch * kSplitLanes) {
+    float2 ml[kBatch];
+    float4 x[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      ml[i] = ml_at(s + i * kSplitLanes);
+      x[i] = o_at(s + i * kSplitLanes);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) absorb(ml[i], x[i]);
   }
-  red_o[tid] = acc;
+  for (; s < n_splits; s += kSplitLanes) absorb(ml_at(s), o_at(s));
+
+  red_m[tid] = M;
   red_l[tid] = L;
+  red_o[tid] = acc;
   __syncthreads();
   for (int off = kSplitLanes / 2; off > 0; off >>= 1) {
     if (sl < off) {
       const int o2 = tid + off * kCols;
-      const float4 y = red_o[o2];
-      red_o[tid].x += y.x; red_o[tid].y += y.y; red_o[tid].z += y.z; red_o[tid].w += y.w;
-      red_l[tid] += red_l[o2];
+      const float m1 = red_m[tid], m2 = red_m[o2];
+      const float mm = fmaxf(m1, m2);
+      const float mu = (mm == -INFINITY) ? 0.f : mm;
+      const float c1 = __builtin_amdgcn_exp2f(m1 - mu), c2 = __builtin_amdgcn_exp2f(m2 - mu);
+      const float4 x1 = red_o[tid], x2 = red_o[o2];
+      red_m[tid] = mm;
+      red_l[tid] = c1 * red_l[tid] + c2 * red_l[o2];
+      red_o[tid] = make_float4(c1 * x1.x + c2 * x2.x, c1 * x1.y + c2 * x2.y, c1 * x1.z + c2 * x2.z,
+                               c1 * x1.w + c2 * x2.w);
     }
     __syncthreads();
   }
@@ -826,7 +850,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, in
     }
     *reinterpret_cast<float4*>(a.out + (size_t)row_id * D + dim0 + col * 4) = res;
     if (col == 0 && blockIdx.y == 0 && a.lse)
-      a.lse[row_id] = (Lt > 0.f) ? (M + log2f(Lt)) * kLn2 : -INFINITY;
+      a.lse[row_id] = (Lt > 0.f) ? (red_m[0] + log2f(Lt)) * kLn2 : -INFINITY;
   }
 }
 

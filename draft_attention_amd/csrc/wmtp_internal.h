@@ -32,7 +32,7 @@ constexpr int kWavesPerBlock = 4;   // wavefronts per workgroup (interleaved til
 #define WMTP_TARGET_BLOCKS_SPLIT 256
 #endif
 #ifndef WMTP_TARGET_BLOCKS_COOP
-#define WMTP_TARGET_BLOCKS_COOP 768
+#define WMTP_TARGET_BLOCKS_COOP 512
 #endif
 #ifndef WMTP_ALLOW_COOP
 #define WMTP_ALLOW_COOP 1

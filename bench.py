@@ -12,7 +12,7 @@ already resident in HBM when timing starts.
 
 Prints ONE JSON line. `value` is the whole step's algorithmic HBM bytes / step time (GB/s).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--graph]
 """
 from __future__ import annotations
 
@@ -28,6 +28,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth
+PROBE_BYTES = 2 << 30  # read-probe buffer (also the source of the backlog reads)
+FLUSH_BYTES = 512 << 20  # twice the 256 MB Infinity Cache
+SWEEP_L = (4096, 16384, 65536, 131072, 262144, 524288, 1048576)
 
 
 def parse():
@@ -36,6 +39,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the context-length sweep of single calls")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each phase of the iteration as a captured HIP graph instead of "
+                         "launching every call from Python")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (reference for "
                          "scaling the HBM byte counters of a profiler) and exit")
@@ -162,59 +170,105 @@ def main():
 
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    rec = {"win_append": [], "win_attn": [], "full_append": [], "full_attn": [],
-           "ver_append": [], "ver_attn": []}
 
-    def one_step(s: int, timed: bool):
-        marks = []
+    # the three phases of a decode iteration, and their attention-only parts
+    def win_phase(s: int, append: bool = True):
         for i in range(k):
             t = s * k + i
-            kn, vn = draft_k[t:t + 1][None], draft_v[t:t + 1][None]
-            e = [ev() for _ in range(5)]
-            e[0].record(stream)
-            W.wmtp_ring_append(ring, kn, vn, 1)
-            e[1].record(stream)
+            if append:
+                W.wmtp_ring_append(ring, draft_k[t:t + 1][None], draft_v[t:t + 1][None], 1)
             W.wmtp_draft_attn_windowed(ring, draft_q[t], Hq, scale3, out3, lse3, ws_win)
-            e[2].record(stream)
-            W.wmtp_ring_append(full, kn, vn, 1)
-            e[3].record(stream)
+
+    def full_phase(s: int, append: bool = True):
+        for i in range(k):
+            t = s * k + i
+            if append:
+                W.wmtp_ring_append(full, draft_k[t:t + 1][None], draft_v[t:t + 1][None], 1)
             W.wmtp_draft_attn_full(full, draft_q[t], Hq, scale3, cap, out3, lse3, ws_full)
-            e[4].record(stream)
-            marks.append(("draft", e))
-        e = [ev() for _ in range(3)]
-        e[0].record(stream)
-        W.wmtp_ring_append(tgt, cand_k[s * m:(s + 1) * m][None], cand_v[s * m:(s + 1) * m][None], m)
-        e[1].record(stream)
+
+    def ver_phase(s: int, append: bool = True):
+        if append:
+            W.wmtp_ring_append(tgt, cand_k[s * m:(s + 1) * m][None],
+                               cand_v[s * m:(s + 1) * m][None], m)
         W.wmtp_verify_attn(tgt, ver_q[s], m, Hq4, scale4, cap4, out4, lse4, ws_ver)
-        e[2].record(stream)
-        marks.append(("verify", e))
-        return marks
+
+    phases = {"win": win_phase, "full": full_phase, "ver": ver_phase}
+    if not args.graph:
+        # every call launched from Python: includes the host's launch latency between calls
+        run = {name: (lambda f: (lambda s, append=True: f(s, append)))(f) for name, f in phases.items()}
+        launch = "eager (one host launch per call)"
+    else:
+        # one HIP graph per phase (captured once, replayed): the kernels of a phase run back to
+        # back on the GPU, as inside a serving engine's captured decode loop. Every replay
+        # appends (the same token bytes) at the next positions, so caches keep growing. On
+        # ROCm 7 the long attention kernels run about 4% slower when launched from a graph than
+        # when launched directly, which is why this is not the default.
+        graphs = {}
+        for name, f in phases.items():
+            for append in (True, False):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    f(0, append)
+                graphs[(name, append)] = g
+        run = {name: (lambda nm: (lambda s, append=True: graphs[(nm, append)].replay()))(name)
+               for name in phases}
+        launch = "hip-graph (one captured graph per phase, replayed)"
 
     log(f"warmup {args.warmup} steps")
     for s in range(args.warmup):
-        one_step(s, False)
+        for name in ("win", "full", "ver"):
+            run[name](s)
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    all_marks = []
+    log(f"timing {args.steps} steps ({launch})")
+    rec = {"win": [], "full": [], "ver": []}
+    marks = []
     start, stop = ev(), ev()
     torch.cuda.synchronize()
     start.record(stream)
     for s in range(args.warmup, total_steps):
-        all_marks.append(one_step(s, True))
+        e = [ev() for _ in range(4)]
+        e[0].record(stream)
+        run["win"](s)
+        e[1].record(stream)
+        run["full"](s)
+        e[2].record(stream)
+        run["ver"](s)
+        e[3].record(stream)
+        marks.append(e)
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    for marks in all_marks:
-        for kind, e in marks:
-            if kind == "draft":
-                rec["win_append"].append(e[0].elapsed_time(e[1]))
-                rec["win_attn"].append(e[1].elapsed_time(e[2]))
-                rec["full_append"].append(e[2].elapsed_time(e[3]))
-                rec["full_attn"].append(e[3].elapsed_time(e[4]))
-            else:
-                rec["ver_append"].append(e[0].elapsed_time(e[1]))
-                rec["ver_attn"].append(e[1].elapsed_time(e[2]))
-    mean_us = {key: 1000.0 * sum(v) / len(v) for key, v in rec.items()}
+    for e in marks:
+        rec["win"].append(e[0].elapsed_time(e[1]))
+        rec["full"].append(e[1].elapsed_time(e[2]))
+        rec["ver"].append(e[2].elapsed_time(e[3]))
+    # attention alone (outside the timed steps): the same phases without the appends, each
+    # enqueued behind a ~0.15 ms read of another buffer so that the host has queued every call
+    # before the GPU reaches the first one (the events then bracket GPU work only)
+    probe_buf = torch.empty(PROBE_BYTES, dtype=torch.uint8, device=dev)
+    probe_out = torch.empty(W.WMTP_PROBE_BLOCKS, dtype=torch.int32, device=dev)
+    backlog = lambda: W.wmtp_probe_read(probe_buf, probe_out, 1 << 30)
+    attn_only = {"win": [], "full": [], "ver": []}
+    for rep in range(max(3, args.steps // 2)):
+        for name in ("win", "full", "ver"):
+            e0, e1 = ev(), ev()
+            backlog()
+            e0.record(stream)
+            run[name]((args.warmup + rep) % total_steps, append=False)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            attn_only[name].append(e0.elapsed_time(e1))
+    read_ceiling = read_probe(W, probe_buf, probe_out, stream, ev)
+    log(f"read probe: {read_ceiling:.1f} GB/s")
+    sweep_res = None if args.no_sweep else sweep(
+        W, synth, D3, full, cap, Hq, scale3, probe_buf, probe_out, stream, ev, log)
+    mean = lambda v: 1000.0 * sum(v) / len(v)
+    mean_us = {
+        "win_step": mean(rec["win"]) / k, "full_step": mean(rec["full"]) / k,
+        "ver_step": mean(rec["ver"]),
+        "win_attn": mean(attn_only["win"]) / k, "full_attn": mean(attn_only["full"]) / k,
+        "ver_attn": mean(attn_only["ver"]),
+    }
 
     # algorithmic HBM bytes (K and V rows read once; q, out, lse; appends read+write the token)
     n_mid = L + k * args.warmup + (k * args.steps) // 2  # mean tokens present during the timed draft
@@ -247,13 +301,13 @@ def main():
                         "(32q/2kv, d128)",
             "context": L, "draft_depth": k, "verify_m": m, "batch": 1,
         },
+        "launch": launch,
         "draft_step_us": {
             "windowed_attn": round(mean_us["win_attn"], 2),
-            "windowed_attn_plus_append": round(mean_us["win_attn"] + mean_us["win_append"], 2),
+            "windowed_attn_plus_append": round(mean_us["win_step"], 2),
             "full_attn": round(mean_us["full_attn"], 2),
-            "full_attn_plus_append": round(mean_us["full_attn"] + mean_us["full_append"], 2),
-            "full_over_windowed": round((mean_us["full_attn"] + mean_us["full_append"]) /
-                                        (mean_us["win_attn"] + mean_us["win_append"]), 1),
+            "full_attn_plus_append": round(mean_us["full_step"], 2),
+            "full_over_windowed": round(mean_us["full_step"] / mean_us["win_step"], 1),
         },
         "hbm_gbs": {
             "windowed_attn": round(gbs(b_win, mean_us["win_attn"]), 1),
@@ -261,11 +315,13 @@ def main():
             "verify_attn": round(gbs(b_ver, mean_us["ver_attn"]), 1),
         },
         "verify_us": {"attn": round(mean_us["ver_attn"], 2),
-                      "append": round(mean_us["ver_append"], 2)},
+                      "attn_plus_append": round(mean_us["ver_step"], 2)},
         "dropped_kv_fraction": round(1.0 - win_slots / n_mid, 5),
+        "read_probe_gbs": round(read_ceiling, 1),
+        "sweep": sweep_res,
         "roofline": {
-            "kernel": "full-context draft attention call (split-K attention + LSE merge), "
-                      "L=1048576, 32q/2kv, d256, bf16",
+            "kernel": "full-context draft attention call (split-K attention + LSE merge, "
+                      "back to back), L=1048576, 32q/2kv, d256, bf16",
             "bound": "hbm",
             "achieved": round(gbs(b_full, mean_us["full_attn"]), 1),
             "peak": PEAK_HBM_GBS,
@@ -282,6 +338,104 @@ def main():
         result["cpu_baseline"] = cpu_baseline(full, tgt, ring, draft_q, ver_q, k, m, S, Wn,
                                               scale3, scale4, step_bytes, log)
     print(json.dumps(result), flush=True)
+
+
+def read_probe(W, buf, out, stream, ev, reps: int = 5) -> float:
+    """GB/s of one streaming read of the whole probe buffer (median of `reps` launches)."""
+    times = []
+    for _ in range(reps + 1):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        W.wmtp_probe_read(buf, out)
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    t = sorted(times[1:])[reps // 2]
+    return buf.numel() / (t * 1e-3) / 1e9
+
+
+def pct(v, q):
+    v = sorted(v)
+    return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+
+
+def sweep(W, synth, D3, full, cap, Hq, scale, probe_buf, probe_out, stream, ev, log,
+          calls: int = 30):
+    """Single draft-step attention calls at the million-token draft shapes over a range of context
+    lengths L (the step attends n = L + 1 tokens): windowed (ring holding sinks + window of the
+    same sequence) and full (the first n rows of the contiguous cache), each timed per call with
+    events, cold (the caches flushed before every call) and warm (calls back to back)."""
+    import torch
+
+    dev = full.k.device
+    Hkv, d, S, Wn = D3.n_kv_heads, D3.head_dim, D3.sink, D3.window
+    dt = full.k.dtype
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    q = synth.queries(D3.seed, 0, 1, 1, Hq, d, dt, dev)
+    out = torch.empty((1, 1, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((1, 1, Hq), dtype=torch.float32, device=dev)
+    ws_full = W.workspace(1, Hq, Hkv, d, 1, cap, dev)
+    ws_win = W.workspace(1, Hq, Hkv, d, 1, S + Wn, dev)
+    res = {"L": [], "n": [], "windowed_slots": [], "full_us_cold": [], "windowed_us_cold": [],
+           "full_us_warm": [], "windowed_us_warm": [], "full_gbs_cold": [],
+           "windowed_gbs_cold": [], "full_over_windowed_cold": []}
+    for L in SWEEP_L:
+        n = L + 1
+        seq = torch.full((1,), n, dtype=torch.int32, device=dev)
+        view = W.KVCache(full.k, full.v, None, seq, 1, Hkv, d, full.capacity, full.capacity, 0,
+                         full.dtype)
+        ring = W.KVCache.ring(1, Hkv, d, S, Wn, dt, dev)
+        for p0, p1 in ((0, min(S, n)), (max(S, n - Wn), n)):
+            if p1 <= p0:
+                continue
+            ring.seq_len.fill_(p0)
+            kn = synth.token_rows(D3.seed, synth.K_ID, 0, p0, p1, Hkv, d, dt, dev)[None]
+            vn = synth.token_rows(D3.seed, synth.V_ID, 0, p0, p1, Hkv, d, dt, dev)[None]
+            W.wmtp_ring_append(ring, kn, vn, p1 - p0)
+        slots = min(n, S + Wn)
+        calls_of = {
+            "full": lambda: W.wmtp_draft_attn_full(view, q, Hq, scale, cap, out, lse, ws_full),
+            "windowed": lambda: W.wmtp_draft_attn_windowed(ring, q, Hq, scale, out, lse, ws_win),
+        }
+        for name, call in calls_of.items():
+            call()
+            cold, warm = [], []
+            for _ in range(calls):
+                e0, e1 = ev(), ev()
+                W.wmtp_llc_flush(flush_buf)
+                e0.record(stream)
+                call()
+                e1.record(stream)
+                cold.append((e0, e1))
+            W.wmtp_probe_read(probe_buf, probe_out, 1 << 30)  # backlog: the host runs ahead
+            marks = [ev() for _ in range(calls + 1)]
+            marks[0].record(stream)
+            for i in range(calls):
+                call()
+                marks[i + 1].record(stream)
+            torch.cuda.synchronize()
+            cold_us = [1000.0 * a.elapsed_time(b) for a, b in cold]
+            warm_us = [1000.0 * marks[i].elapsed_time(marks[i + 1]) for i in range(calls)]
+            res[f"{name}_us_cold"].append({"p50": round(pct(cold_us, 0.5), 2),
+                                           "p10": round(pct(cold_us, 0.1), 2),
+                                           "p90": round(pct(cold_us, 0.9), 2)})
+            res[f"{name}_us_warm"].append({"p50": round(pct(warm_us, 0.5), 2),
+                                           "p10": round(pct(warm_us, 0.1), 2),
+                                           "p90": round(pct(warm_us, 0.9), 2)})
+        rows = {"full": n, "windowed": slots}
+        for name in ("full", "windowed"):
+            nbytes = 2 * rows[name] * Hkv * d * 2 + Hq * d * 2 + Hq * (d + 1) * 4
+            t = res[f"{name}_us_cold"][-1]["p50"]
+            res[f"{name}_gbs_cold"].append(round(nbytes / (t * 1e-6) / 1e9, 1))
+        res["full_over_windowed_cold"].append(
+            round(res["full_us_cold"][-1]["p50"] / res["windowed_us_cold"][-1]["p50"], 2))
+        res["L"].append(L)
+        res["n"].append(n)
+        res["windowed_slots"].append(slots)
+        log(f"sweep L={L}: full {res['full_us_cold'][-1]['p50']} us, windowed "
+            f"{res['windowed_us_cold'][-1]['p50']} us (cold p50)")
+        del ring
+    return res
 
 
 def cpu_baseline(full, tgt, ring, draft_q, ver_q, k, m, S, Wn, scale3, scale4, step_bytes, log):

@@ -16,6 +16,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwmtp.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "wmtp.h")
+HEADERS = [HEADER, os.path.join(os.path.dirname(_HERE), "include", "wmtp_probe.h")]
 
 WMTP_OK = 0
 WMTP_ERR_INVALID_ARG = 1
@@ -62,16 +63,18 @@ def lib():
         L.wmtp_attn_workspace_bytes.restype = sz
         L.wmtp_status_string.argtypes = [ctypes.c_int]
         L.wmtp_status_string.restype = ctypes.c_char_p
+        L.wmtp_probe_read.argtypes = [vp, sz, vp, vp]
+        L.wmtp_llc_flush.argtypes = [vp, sz, ctypes.c_uint8, vp]
         for name in ("wmtp_ring_append", "wmtp_draft_attn_windowed", "wmtp_draft_attn_full",
-                     "wmtp_verify_attn"):
+                     "wmtp_verify_attn", "wmtp_probe_read", "wmtp_llc_flush"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
 
 
 def header_functions():
-    """Names of the functions include/wmtp.h declares."""
-    text = open(HEADER).read()
+    """Names of the functions include/wmtp.h and include/wmtp_probe.h declare."""
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(wmtp_\w+)\s*\(", text, re.M)))
 
 
@@ -246,6 +249,26 @@ def wmtp_verify_attn(cache, q, m: int, n_q_heads: int, sm_scale: float, max_seq_
                                 float(sm_scale), int(max_seq_len), _ptr(out), _ptr(lse),
                                 _ptr(ws), int(nbytes), _stream(stream))
     return _done(st, "wmtp_verify_attn", check)
+
+
+WMTP_PROBE_BLOCKS = 512  # include/wmtp_probe.h
+
+
+def wmtp_probe_read(buf, out, nbytes: Optional[int] = None, stream=None, check=True) -> int:
+    """Stream `nbytes` (default: all) of `buf` once; out gets WMTP_PROBE_BLOCKS uint32 XORs."""
+    _numel_ok(out, WMTP_PROBE_BLOCKS, 4, "out")
+    n = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    if not isinstance(buf, int) and n > buf.numel() * buf.element_size():
+        raise ValueError("wmtp: nbytes exceeds the buffer")
+    st = lib().wmtp_probe_read(_ptr(buf), int(n), _ptr(out), _stream(stream))
+    return _done(st, "wmtp_probe_read", check)
+
+
+def wmtp_llc_flush(buf, value: int = 0, stream=None, check=True) -> int:
+    """Overwrite all of `buf` with the byte `value` (evicts earlier calls' lines from the caches)."""
+    n = buf.numel() * buf.element_size()
+    st = lib().wmtp_llc_flush(_ptr(buf), int(n), int(value) & 0xFF, _stream(stream))
+    return _done(st, "wmtp_llc_flush", check)
 
 
 def wmtp_attn_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, m: int,

@@ -30,7 +30,8 @@ def _kv(**kw):
 def test_exports_every_declared_function(lib):
     names = W.header_functions()
     assert set(names) == {"wmtp_ring_append", "wmtp_draft_attn_windowed", "wmtp_draft_attn_full",
-                          "wmtp_verify_attn", "wmtp_attn_workspace_bytes", "wmtp_status_string"}
+                          "wmtp_verify_attn", "wmtp_attn_workspace_bytes", "wmtp_status_string",
+                          "wmtp_probe_read", "wmtp_llc_flush"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -132,3 +133,15 @@ def test_workspace_bytes(lib):
     # the split-K partials stay a small fraction of the K/V bytes a full 1M-token read streams
     kv_bytes = 2 * 2 * 1048581 * 256 * 2
     assert big < 0.05 * kv_bytes
+
+
+def test_probe_arguments_rejected_before_launch(lib):
+    out = FAKE
+    assert lib.wmtp_probe_read(None, 1024, out, None) == W.WMTP_ERR_INVALID_ARG
+    assert lib.wmtp_probe_read(FAKE, 0, out, None) == W.WMTP_ERR_INVALID_ARG
+    assert lib.wmtp_probe_read(FAKE, 1000, out, None) == W.WMTP_ERR_INVALID_ARG  # not 16-byte sized
+    assert lib.wmtp_probe_read(FAKE + 8, 1024, out, None) == W.WMTP_ERR_INVALID_ARG
+    assert lib.wmtp_probe_read(FAKE, 1024, None, None) == W.WMTP_ERR_INVALID_ARG
+    assert lib.wmtp_llc_flush(None, 1024, 0, None) == W.WMTP_ERR_INVALID_ARG
+    assert lib.wmtp_llc_flush(FAKE, 24, 0, None) == W.WMTP_ERR_INVALID_ARG
+    assert lib.wmtp_llc_flush(FAKE + 4, 1024, 0, None) == W.WMTP_ERR_INVALID_ARG

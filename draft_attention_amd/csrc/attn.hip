@@ -124,7 +124,11 @@ template <int D, int NR, bool BF16>
 struct QOperand {
   using F = Frag<D, BF16>;
   typedef typename std::conditional<BF16, bf16x8_t, f32x4_t>::type Vec;
+#ifdef WMTP_WIDE_QREG
+  static constexpr bool kInLds = false;
+#else
   static constexpr bool kInLds = NR * F::kQRegs * 4 >= 64;
+#endif
   Vec reg[kInLds ? 1 : NR][kInLds ? 1 : F::kQRegs];
   const uint4* lds;
   int lane;
@@ -178,7 +182,10 @@ __device__ __forceinline__ void compute_tile(const Tile<D, BF16>& T, const QOper
   // The weights are taken relative to a reference maximum st.m that only moves when a tile's
   // maximum exceeds it by more than kRescaleLog2 (softmax does not depend on the reference), so
   // the weights stay below 2^kRescaleLog2 and the O accumulators are rescaled only on the rare
-  // tiles where some row's reference moves (a wavefront-uniform branch).
+  // tiles where some row's reference moves (a wavefront-uniform branch). Each lane first tests
+  // its own four keys; only when one of them passes the threshold does the wavefront take the
+  // row maximum over the row's four lanes (no cross-lane traffic on the common path; the outcome
+  // is the same as testing the row maximum on every tile).
   float sc[NR][4];
   bool need = false;
   float mx[NR];
@@ -192,12 +199,13 @@ __device__ __forceinline__ void compute_tile(const Tile<D, BF16>& T, const QOper
       sc[rb][j] = (key <= vis) ? s[rb][j] * scale_log2 : -INFINITY;
       m = fmaxf(m, sc[rb][j]);
     }
-    mx[rb] = xgroup_max(m);
-    need |= mx[rb] > st.m[rb] + kRescaleLog2;
+    mx[rb] = m;
+    need |= m > st.m[rb] + kRescaleLog2;
   }
   if (__ballot(need)) {
 #pragma unroll
     for (int rb = 0; rb < NR; ++rb) {
+      mx[rb] = xgroup_max(mx[rb]);
       // rows whose reference stays put keep alpha = 1 exactly (their st.m may still be -inf
       // when the causal mask hid every key so far, and -inf - -inf is not a number)
       const bool moved = mx[rb] > st.m[rb] + kRescaleLog2;
@@ -284,6 +292,9 @@ constexpr bool pipelined() {
   constexpr int q = QOperand<D, NR, BF16>::kInLds ? 0 : NR * F::kQRegs * 4;
   constexpr int o = NR * F::kBlocks * 4;
   constexpr int tile = F::kQRegs * 4 + 4 * F::kSets * F::kVWords;
+#ifdef WMTP_WIDE
+  if (NR == 4 && D == 128 && BF16) return true;
+#endif
   return q + o + 2 * tile <= 224 && o <= 96;
 }
 
@@ -476,8 +487,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
 // Cooperative-tile kernel. The four wavefronts of a workgroup consume the SAME 16-key tile, which
 // the whole workgroup stages through LDS: every thread issues fully coalesced 16-byte loads for its
 // share of the tile (K and V rows are contiguous in HBM), keeps kPrefetch tiles of them in flight
-// in registers, and writes the oldest one into a double-buffered LDS stage (16-byte chunks XOR-
-// swizzled by key so the operand reads below are bank-conflict free). One barrier per tile.
+// in registers, and writes the oldest one into a double-buffered LDS stage (K chunks XOR-swizzled
+// by key so the operand reads below are bank-conflict free). One barrier per tile.
 // The wavefronts split the work of a tile either by query-row block (NB = 4 blocks of 16 rows, the
 // verify shape) or by output dimensions (NB = 1: each wavefront owns D/4 dims of all 16 rows and
 // recomputes the 16x16 score tile, which is cheap on the matrix cores). Each wavefront writes its
@@ -509,19 +520,27 @@ struct Coop {
   static_assert(kDpl >= (BF16 ? 2 : 1), "each lane needs a pair of bf16 dims");
 };
 
+// Byte offset of 16-byte chunk `chunk` of key `key` in a staged K (tensor 0) or V (tensor 1) tile.
+// K chunks are XOR-swizzled by key: the S^T operand read takes 16 keys' chunk ks*4+grp in one
+// instruction, which would otherwise fall into the same banks (measured on MI355X: 28 conflict
+// cycles per read unswizzled, none swizzled). V is stored plainly: its reads take consecutive
+// chunks of one key per 16 lanes, conflict-free as they are (and 4 conflict cycles per read with
+// the K swizzle applied).
 template <int D, int NB, bool BF16>
-__device__ __forceinline__ int coop_slot(int key, int chunk) {
+__device__ __forceinline__ int coop_slot(int key, int chunk, int tensor) {
   using C = Coop<D, NB, BF16>;
-  return key * C::kRowBytes + ((chunk ^ (key & C::kSwz)) << 4);
+  return key * C::kRowBytes + ((chunk ^ (tensor ? 0 : (key & C::kSwz))) << 4);
 }
 
 template <int D, int NB, bool BF16>
-__global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int n_splits,
+#ifndef WMTP_COOP_WPC
+#define WMTP_COOP_WPC 2
+#endif
+__global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(AttnArgs a, int n_splits,
                                                                  int n_chunks, int chunk_rows) {
   using C = Coop<D, NB, BF16>;
   typedef typename std::conditional<BF16, bf16x8_t, f32x4_t>::type QVec;
   __shared__ __attribute__((aligned(16))) char sm_tile[2][C::kStageBytes];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -544,7 +563,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int 
   n = min(n, a.limit);
   const int last = n - 1;
   const int tiles = (n + kTileKeys - 1) / kTileKeys;
+  // Addresses only depend on the host-side bound a.limit (>= 1), so the first tiles are requested
+  // without waiting for seq_len; seq_len only masks (a tile past it is computed fully masked).
+  const int tiles_lim = (a.limit + kTileKeys - 1) / kTileKeys;
+  const int last_lim = a.limit - 1;
   const int my_tiles = split < tiles ? (tiles - split + n_splits - 1) / n_splits : 0;
+  auto tile_start = [&](int i) {  // first key of the workgroup's i-th tile, clamped into range
+    const int tl = split + i * n_splits;
+    return (tl < tiles_lim ? tl : tiles_lim - 1) * kTileKeys;
+  };
+  const bool has_range = split < tiles_lim;
   const int my_stages = (my_tiles + C::kTps - 1) / C::kTps;
 
   const size_t head_off = (size_t)(b * a.n_kv_heads + h) * (size_t)a.capacity * C::kRowBytes;
@@ -554,14 +582,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int 
   // staging: load l of this thread is chunk q = tid + kThreads*l of the stage: tile q / (32*kChunks),
   // then K chunks before V chunks
   uint4 stg[C::kPrefetch][C::kLoads];
-  // Addresses only depend on the host-side bound a.limit (>= 1), so the first tiles are requested
-  // without waiting for seq_len; seq_len only masks (a tile past it is computed fully masked).
-  const int tiles_lim = (a.limit + kTileKeys - 1) / kTileKeys;
-  const int last_lim = a.limit - 1;
-  auto tile_start = [&](int i) {  // first key of the workgroup's i-th tile, clamped into range
-    const int tl = split + i * n_splits;
-    return (tl < tiles_lim ? tl : tiles_lim - 1) * kTileKeys;
-  };
   auto load_stage = [&](uint4(&dst)[C::kLoads], int stage) {
 #pragma unroll
     for (int l = 0; l < C::kLoads; ++l) {
@@ -583,7 +603,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int 
       const int key = (q / C::kChunks) % 16;
       const int c = q % C::kChunks;
       *reinterpret_cast<uint4*>(&sm_tile[buf][(2 * u + tensor) * C::kTileBytes +
-                                              coop_slot<D, NB, BF16>(key, c)]) = src[l];
+                                              coop_slot<D, NB, BF16>(key, c, tensor)]) = src[l];
     }
   };
 
@@ -608,7 +628,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int 
                                                 (ks * 4 + grp) * 16));
   }
 
-  if (split < tiles_lim) {
+  if (has_range) {
 #pragma unroll
     for (int s = 0; s < C::kPrefetch; ++s) load_stage(stg[s], s);
   }
@@ -619,6 +639,102 @@ __global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int 
   f32x4_t o[C::kDpl];
 #pragma unroll
   for (int e = 0; e < C::kDpl; ++e) o[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // one 16-key tile: K at kt, V at kt + kTileBytes (swizzled LDS layout); i = the workgroup's
+  // tile index (tiles past its share are computed fully masked)
+  auto tile_step = [&](const char* kt, int i) {
+    const bool live = i < my_tiles;  // workgroup-uniform
+    const int t0 = tile_start(i);
+    const char* vt = kt + C::kTileBytes;
+    // ---- S^T (16 keys x 16 rows) for this row block
+    f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::kQRegs; ++ks) {
+      const uint4 kv =
+          *reinterpret_cast<const uint4*>(kt + coop_slot<D, NB, BF16>(r16, ks * 4 + grp, 0));
+      if constexpr (BF16) {
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qf[ks],
+                                                       sacc, 0, 0, 0);
+      } else {
+        const float4 kf = __builtin_bit_cast(float4, kv);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.x, qf[ks][0], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.y, qf[ks][1], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.z, qf[ks][2], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.w, qf[ks][3], sacc, 0, 0, 0);
+      }
+    }
+
+    // ---- softmax with a lazily moved reference max (as in the split kernel)
+    const int vis = live ? min(last, last_visible) : -1;
+    float sc[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = t0 + 4 * grp + j;
+      sc[j] = (key <= vis) ? sacc[j] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, sc[j]);
+    }
+    if (__ballot(mx > m_ref + kRescaleLog2)) {  // lane-local test first, as in the split kernel
+      mx = xgroup_max(mx);
+      const bool moved = mx > m_ref + kRescaleLog2;
+      const float alpha = moved ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;
+      l_lane *= alpha;
+#pragma unroll
+      for (int e = 0; e < C::kDpl; ++e) o[e] *= alpha;
+      m_ref = moved ? mx : m_ref;
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = __builtin_amdgcn_exp2f(sc[j] - m_use);
+      l_lane += p[j];
+    }
+
+    // ---- O^T (this wavefront's dims) += V^T . P^T; lane r16 owns dims d0 + kDpl*r16 + e
+    constexpr int kVBytes = C::kDpl * C::kEB;  // bytes per key per lane
+    constexpr int kVWords = kVBytes / 4;
+    uint32_t vw[4][kVWords];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int key = 4 * grp + t;
+      const int bo = (d0 + C::kDpl * r16) * C::kEB;  // byte offset in the key row
+#pragma unroll
+      for (int w = 0; w < kVWords; w += (kVWords >= 4 ? 4 : kVWords)) {
+        const int byte = bo + 4 * w;
+        const char* src = vt + key * C::kRowBytes + byte;
+        if constexpr (kVWords >= 4) {
+          const uint4 x = *reinterpret_cast<const uint4*>(src);
+          vw[t][w] = x.x; vw[t][w + 1] = x.y; vw[t][w + 2] = x.z; vw[t][w + 3] = x.w;
+        } else if constexpr (kVWords == 2) {
+          const uint2 x = *reinterpret_cast<const uint2*>(src);
+          vw[t][0] = x.x; vw[t][1] = x.y;
+        } else {
+          vw[t][0] = *reinterpret_cast<const uint32_t*>(src);
+        }
+      }
+    }
+    if constexpr (BF16) {
+      const bf16x4_t pb = __builtin_convertvector(f32x4_t{p[0], p[1], p[2], p[3]}, bf16x4_t);
+      const s16x4_t pop = __builtin_bit_cast(s16x4_t, pb);
+#pragma unroll
+      for (int w = 0; w < kVWords; ++w)
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) {
+          const uint32_t k01 = pack_halves(vw[0][w], vw[1][w], hi);
+          const uint32_t k23 = pack_halves(vw[2][w], vw[3][w], hi);
+          const s16x4_t vop = __builtin_bit_cast(s16x4_t, make_uint2(k01, k23));
+          o[2 * w + hi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, o[2 * w + hi], 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < C::kDpl; ++e)
+          o[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, vw[u][e]), p[u],
+                                                      o[e], 0, 0, 0);
+    }
+  };
 
   // Rounds of exactly kPrefetch tiles with no early exit: tiles past the workgroup's share are
   // computed fully masked. The straight-line round lets the compiler wait for exactly the oldest
@@ -632,102 +748,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_coop_kernel(AttnArgs a, int 
       load_stage(stg[s], st + C::kPrefetch);
       __syncthreads();  // stage st visible; every wavefront is done with stage st-1's buffer
 #pragma unroll
-      for (int u = 0; u < C::kTps; ++u) {
-      const int i = st * C::kTps + u;
-      const bool live = i < my_tiles;  // workgroup-uniform
-      const int t0 = tile_start(i);
-      const char* kt = sm_tile[buf] + 2 * u * C::kTileBytes;
-      const char* vt = kt + C::kTileBytes;
-
-      // ---- S^T (16 keys x 16 rows) for this row block
-      f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < C::kQRegs; ++ks) {
-        const uint4 kv =
-            *reinterpret_cast<const uint4*>(kt + coop_slot<D, NB, BF16>(r16, ks * 4 + grp));
-        if constexpr (BF16) {
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qf[ks],
-                                                         sacc, 0, 0, 0);
-        } else {
-          const float4 kf = __builtin_bit_cast(float4, kv);
-          sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.x, qf[ks][0], sacc, 0, 0, 0);
-          sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.y, qf[ks][1], sacc, 0, 0, 0);
-          sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.z, qf[ks][2], sacc, 0, 0, 0);
-          sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.w, qf[ks][3], sacc, 0, 0, 0);
-        }
-      }
-
-      // ---- softmax with a lazily moved reference max (see compute_tile)
-      const int vis = live ? min(last, last_visible) : -1;
-      float sc[4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = t0 + 4 * grp + j;
-        sc[j] = (key <= vis) ? sacc[j] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sc[j]);
-      }
-      mx = xgroup_max(mx);
-      const bool moved = mx > m_ref + kRescaleLog2;
-      if (__ballot(moved)) {
-        const float alpha = moved ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;
-        l_lane *= alpha;
-#pragma unroll
-        for (int e = 0; e < C::kDpl; ++e) o[e] *= alpha;
-        m_ref = moved ? mx : m_ref;
-      }
-      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-      float p[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(sc[j] - m_use);
-        l_lane += p[j];
-      }
-
-      // ---- O^T (this wavefront's dims) += V^T . P^T; lane r16 owns dims d0 + kDpl*r16 + e
-      constexpr int kVBytes = C::kDpl * C::kEB;  // bytes per key per lane
-      constexpr int kVWords = kVBytes / 4;
-      uint32_t vw[4][kVWords];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int key = 4 * grp + t;
-        const int bo = (d0 + C::kDpl * r16) * C::kEB;  // byte offset in the key row
-#pragma unroll
-        for (int w = 0; w < kVWords; w += (kVWords >= 4 ? 4 : kVWords)) {
-          const int byte = bo + 4 * w;
-          const char* src = vt + coop_slot<D, NB, BF16>(key, byte >> 4) + (byte & 15);
-          if constexpr (kVWords >= 4) {
-            const uint4 x = *reinterpret_cast<const uint4*>(src);
-            vw[t][w] = x.x; vw[t][w + 1] = x.y; vw[t][w + 2] = x.z; vw[t][w + 3] = x.w;
-          } else if constexpr (kVWords == 2) {
-            const uint2 x = *reinterpret_cast<const uint2*>(src);
-            vw[t][0] = x.x; vw[t][1] = x.y;
-          } else {
-            vw[t][0] = *reinterpret_cast<const uint32_t*>(src);
-          }
-        }
-      }
-      if constexpr (BF16) {
-        const bf16x4_t pb = __builtin_convertvector(f32x4_t{p[0], p[1], p[2], p[3]}, bf16x4_t);
-        const s16x4_t pop = __builtin_bit_cast(s16x4_t, pb);
-#pragma unroll
-        for (int w = 0; w < kVWords; ++w)
-#pragma unroll
-          for (int hi = 0; hi < 2; ++hi) {
-            const uint32_t k01 = pack_halves(vw[0][w], vw[1][w], hi);
-            const uint32_t k23 = pack_halves(vw[2][w], vw[3][w], hi);
-            const s16x4_t vop = __builtin_bit_cast(s16x4_t, make_uint2(k01, k23));
-            o[2 * w + hi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, o[2 * w + hi], 0, 0, 0);
-          }
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int e = 0; e < C::kDpl; ++e)
-            o[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, vw[u][e]), p[u],
-                                                        o[e], 0, 0, 0);
-      }
-      }
+      for (int u = 0; u < C::kTps; ++u)
+        tile_step(sm_tile[buf] + 2 * u * C::kTileBytes, st * C::kTps + u);
     }
   }
 
@@ -764,7 +786,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, in
                                                     int chunk_rows, int nr) {
   constexpr int kCols = 16;
   constexpr int kSplitLanes = 256 / kCols;
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
   __shared__ float red_m[256];
   __shared__ float4 red_o[256];
   __shared__ float red_l[256];
@@ -807,19 +829,21 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, in
     L += w * ml.y;
     acc.x += w * x.x; acc.y += w * x.y; acc.z += w * x.z; acc.w += w * x.w;
   };
-  int s = sl;
-  for (; s + (kBatch - 1) * kSplitLanes < n_splits; s += kBatch * kSplitLanes) {
+  // batches of kBatch partials per lane, all loads of a batch in flight together (one batch covers
+  // up to 256 splits); indices past the last split re-read it and are not absorbed
+  for (int s0 = sl; s0 < n_splits; s0 += kBatch * kSplitLanes) {
     float2 ml[kBatch];
     float4 x[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      ml[i] = ml_at(s + i * kSplitLanes);
-      x[i] = o_at(s + i * kSplitLanes);
+      const int si = min(s0 + i * kSplitLanes, n_splits - 1);
+      ml[i] = ml_at(si);
+      x[i] = o_at(si);
     }
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) absorb(ml[i], x[i]);
+    for (int i = 0; i < kBatch; ++i)
+      if (s0 + i * kSplitLanes < n_splits) absorb(ml[i], x[i]);
   }
-  for (; s < n_splits; s += kSplitLanes) absorb(ml_at(s), o_at(s));
 
   red_m[tid] = M;
   red_l[tid] = L;

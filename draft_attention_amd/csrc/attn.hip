@@ -499,6 +499,7 @@ struct Coop {
   static constexpr int kRowBytes = D * kEB;
   static constexpr int kChunks = kRowBytes / 16;             // 16-byte chunks per key row
   static constexpr int kSwz = (kChunks < 16 ? kChunks : 16) - 1;
+  static constexpr int kVSwz = (kChunks / 2 < 8 ? kChunks / 2 : 8) - 1;  // 32-byte segments of V
   static constexpr int kSplitD = kWavesPerBlock / NB;         // wavefronts sharing a row block
   static constexpr int kDw = D / kSplitD;                     // output dims per wavefront
   static constexpr int kDpl = kDw / 16;                       // V dims per lane (= output blocks)
@@ -523,13 +524,16 @@ struct Coop {
 // Byte offset of 16-byte chunk `chunk` of key `key` in a staged K (tensor 0) or V (tensor 1) tile.
 // K chunks are XOR-swizzled by key: the S^T operand read takes 16 keys' chunk ks*4+grp in one
 // instruction, which would otherwise fall into the same banks (measured on MI355X: 28 conflict
-// cycles per read unswizzled, none swizzled). V is stored plainly: its reads take consecutive
-// chunks of one key per 16 lanes, conflict-free as they are (and 4 conflict cycles per read with
-// the K swizzle applied).
+// cycles per read unswizzled, none swizzled). bf16 V is read with transposing reads in which each
+// 16-lane group takes the same 32-byte segment of four consecutive keys; its 32-byte segments are
+// XOR-swizzled by (key & 7) so that eight consecutive keys' segments cover all banks. fp32 V is
+// read one key row per 16 lanes and stays plain (conflict-free as it is).
 template <int D, int NB, bool BF16>
 __device__ __forceinline__ int coop_slot(int key, int chunk, int tensor) {
   using C = Coop<D, NB, BF16>;
-  return key * C::kRowBytes + ((chunk ^ (tensor ? 0 : (key & C::kSwz))) << 4);
+  if (tensor == 0) return key * C::kRowBytes + ((chunk ^ (key & C::kSwz)) << 4);
+  if constexpr (BF16) return key * C::kRowBytes + ((chunk ^ (2 * (key & C::kVSwz))) << 4);
+  return key * C::kRowBytes + (chunk << 4);
 }
 
 template <int D, int NB, bool BF16>
@@ -618,6 +622,8 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   const int jq = row_q / G;
   const int hq = h * G + row_q % G;
   const int last_visible = (a.mode == kModeVerify) ? (n - a.m + jq) : (n - 1);
+  // the last key every row of the workgroup may attend (candidate 0 sees the fewest)
+  const int vis_all = min(last, (a.mode == kModeVerify) ? (n - a.m) : (n - 1));
   QVec qf[C::kQRegs];
   {
     const size_t qoff = ((size_t)(b * a.m + jq) * a.n_q_heads + hq) * D;
@@ -668,11 +674,19 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
     const int vis = live ? min(last, last_visible) : -1;
     float sc[4];
     float mx = -INFINITY;
+    if (live && t0 + kTileKeys - 1 <= vis_all) {  // workgroup-uniform: no key of the tile masked
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = t0 + 4 * grp + j;
-      sc[j] = (key <= vis) ? sacc[j] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sc[j]);
+      for (int j = 0; j < 4; ++j) {
+        sc[j] = sacc[j] * scale_log2;
+        mx = fmaxf(mx, sc[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = t0 + 4 * grp + j;
+        sc[j] = (key <= vis) ? sacc[j] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sc[j]);
+      }
     }
     if (__ballot(mx > m_ref + kRescaleLog2)) {  // lane-local test first, as in the split kernel
       mx = xgroup_max(mx);
@@ -691,42 +705,43 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
       l_lane += p[j];
     }
 
-    // ---- O^T (this wavefront's dims) += V^T . P^T; lane r16 owns dims d0 + kDpl*r16 + e
-    constexpr int kVBytes = C::kDpl * C::kEB;  // bytes per key per lane
-    constexpr int kVWords = kVBytes / 4;
-    uint32_t vw[4][kVWords];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int key = 4 * grp + t;
-      const int bo = (d0 + C::kDpl * r16) * C::kEB;  // byte offset in the key row
-#pragma unroll
-      for (int w = 0; w < kVWords; w += (kVWords >= 4 ? 4 : kVWords)) {
-        const int byte = bo + 4 * w;
-        const char* src = vt + key * C::kRowBytes + byte;
-        if constexpr (kVWords >= 4) {
-          const uint4 x = *reinterpret_cast<const uint4*>(src);
-          vw[t][w] = x.x; vw[t][w + 1] = x.y; vw[t][w + 2] = x.z; vw[t][w + 3] = x.w;
-        } else if constexpr (kVWords == 2) {
-          const uint2 x = *reinterpret_cast<const uint2*>(src);
-          vw[t][0] = x.x; vw[t][1] = x.y;
-        } else {
-          vw[t][0] = *reinterpret_cast<const uint32_t*>(src);
-        }
-      }
-    }
+    // ---- O^T (this wavefront's dims) += V^T . P^T
     if constexpr (BF16) {
+      // Block e covers dims d0 + 16e .. +15. The V^T operand (lane (r16, grp): keys 4*grp .. +3
+      // of dim d0 + 16e + r16) comes from one transposing LDS read per block: within each 16-lane
+      // group, lane 4j + q addresses the 8 bytes of key 4*grp + j at dims d0 + 16e + 4q .. +3,
+      // and lane i receives element i % 4 of what lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4 address.
       const bf16x4_t pb = __builtin_convertvector(f32x4_t{p[0], p[1], p[2], p[3]}, bf16x4_t);
       const s16x4_t pop = __builtin_bit_cast(s16x4_t, pb);
+      const int vkey = 4 * grp + (r16 >> 2);
 #pragma unroll
-      for (int w = 0; w < kVWords; ++w)
-#pragma unroll
-        for (int hi = 0; hi < 2; ++hi) {
-          const uint32_t k01 = pack_halves(vw[0][w], vw[1][w], hi);
-          const uint32_t k23 = pack_halves(vw[2][w], vw[3][w], hi);
-          const s16x4_t vop = __builtin_bit_cast(s16x4_t, make_uint2(k01, k23));
-          o[2 * w + hi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, o[2 * w + hi], 0, 0, 0);
-        }
+      for (int e = 0; e < C::kDpl; ++e) {
+        const int c = ((d0 + 16 * e) >> 3) + ((r16 >> 1) & 1);
+        const char* src = vt + coop_slot<D, NB, BF16>(vkey, c, 1) + (r16 & 1) * 8;
+        typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+        const s16x4_t vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(__attribute__((address_space(3))) const char*)src);
+        o[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, o[e], 0, 0, 0);
+      }
     } else {
+      // lane r16 owns dims d0 + kDpl*r16 + e: one key row's kDpl consecutive dims per lane
+      uint32_t vw[4][C::kDpl];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const char* src = vt + (4 * grp + t) * C::kRowBytes + (d0 + C::kDpl * r16) * C::kEB;
+#pragma unroll
+        for (int w = 0; w < C::kDpl; w += (C::kDpl >= 4 ? 4 : C::kDpl)) {
+          if constexpr (C::kDpl >= 4) {
+            const uint4 x = *reinterpret_cast<const uint4*>(src + 4 * w);
+            vw[t][w] = x.x; vw[t][w + 1] = x.y; vw[t][w + 2] = x.z; vw[t][w + 3] = x.w;
+          } else if constexpr (C::kDpl == 2) {
+            const uint2 x = *reinterpret_cast<const uint2*>(src);
+            vw[t][0] = x.x; vw[t][1] = x.y;
+          } else {
+            vw[t][0] = *reinterpret_cast<const uint32_t*>(src);
+          }
+        }
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -760,17 +775,24 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   constexpr int kRows = 16 * NB;
   const int rloc = rb * 16 + r16;
   float* dst = a.ws_o + (part * kRows + rloc) * D + d0;
-  // lane (r16, grp) holds O^T rows 4*grp + j of block e: dim d0 + kDpl*(4*grp + j) + e
+  if constexpr (BF16) {
+    // lane (r16, grp) holds O^T rows 4*grp + j of block e: dims d0 + 16e + 4*grp + j
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float* d = dst + C::kDpl * (4 * grp + j);
-    if constexpr (C::kDpl >= 4) {
+    for (int e = 0; e < C::kDpl; ++e)
+      *reinterpret_cast<float4*>(dst + 16 * e + 4 * grp) = make_float4(o[e][0], o[e][1], o[e][2], o[e][3]);
+  } else {
+    // lane (r16, grp) holds O^T rows 4*grp + j of block e: dim d0 + kDpl*(4*grp + j) + e
 #pragma unroll
-      for (int e = 0; e < C::kDpl; e += 4)
-        *reinterpret_cast<float4*>(d + e) = make_float4(o[e][j], o[e + 1][j], o[e + 2][j], o[e + 3][j]);
-    } else {
+    for (int j = 0; j < 4; ++j) {
+      float* d = dst + C::kDpl * (4 * grp + j);
+      if constexpr (C::kDpl >= 4) {
 #pragma unroll
-      for (int e = 0; e < C::kDpl; ++e) d[e] = o[e][j];
+        for (int e = 0; e < C::kDpl; e += 4)
+          *reinterpret_cast<float4*>(d + e) = make_float4(o[e][j], o[e + 1][j], o[e + 2][j], o[e + 3][j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < C::kDpl; ++e) d[e] = o[e][j];
+      }
     }
   }
   if (d0 == 0 && grp == 0)

@@ -27,6 +27,12 @@ here (listed with reasons in the design notes of the repository):
 * GQA: query head hq reads KV head hq // G with G = Hq / Hkv;
 * ring slot of position p: p for p < S, else S + (p - S) mod W (the first window token lands in
   slot S); a contiguous cache is the same map with S = capacity, W = 0;
+* a ring may carry ``slack`` extra window slots (positions wrap over W + slack slots, the draft
+  still attends the last W): up to ``slack`` newest tokens can then be discarded after a
+  rejection, the MASW page's rollback of speculative local KV (section 4.3), read as
+  "restore exactly the state before the rejected tokens were appended";
+* greedy acceptance: draft token i is kept while it equals the target's argmax at row i (lowest
+  index on ties); the target's argmax at the first rejected row is the next token;
 * verification query j of m (the candidates sit at positions n-m .. n-1) attends positions
   0 .. n-m+j, its own included;
 * outputs and lse are float64 here; lse uses the natural log; an empty set gives o = 0 and
@@ -142,29 +148,90 @@ def ring_slot(p, S: int, W: int):
 
 
 class RingModel:
-    """Host simulation of every append into per-sequence ring buffers of S + W slots.
+    """Host simulation of every append into per-sequence ring buffers of S + W + slack slots.
 
-    ``tags[b, s]`` is the logical position held in slot s of sequence b (-1: never written),
-    ``n[b]`` the number of tokens appended so far. Appends are applied token by token in
-    position order, so a later token always overwrites an earlier one in the same slot.
+    ``tags[b, s]`` is the logical position held in slot s of sequence b (-1: never written or
+    discarded), ``n[b]`` the number of tokens present. Window positions wrap over W + slack slots
+    (slack = 0 is the compact ring of the abstract's last sentence); the draft attends the sinks and
+    the last W positions only, so up to ``slack`` speculative tokens can be discarded again
+    (:meth:`rollback`) without having overwritten a position the window still needs. Appends are
+    applied token by token in position order, so a later token always overwrites an earlier one in
+    the same slot.
     """
 
-    def __init__(self, batch: int, S: int, W: int):
-        self.S, self.W = S, W
-        self.tags = np.full((batch, S + W), -1, dtype=np.int64)
+    def __init__(self, batch: int, S: int, W: int, slack: int = 0):
+        if slack < 0:
+            raise ValueError("slack must be >= 0")
+        self.S, self.W, self.slack = S, W, slack
+        self.Wp = W + slack  # window slots
+        self.tags = np.full((batch, S + self.Wp), -1, dtype=np.int64)
         self.n = np.zeros(batch, dtype=np.int64)
 
     def append(self, b: int, count: int) -> None:
         if count <= 0:
             return
         p = np.arange(self.n[b], self.n[b] + count, dtype=np.int64)
-        s = ring_slot(p, self.S, self.W)
-        # positions increase, so "last writer wins" is the per-slot maximum
+        s = ring_slot(p, self.S, self.Wp)
+        # positions increase, so "last writer wins" is the per-slot maximum over what is there now
+        # (a discarded slot holds -1)
         np.maximum.at(self.tags[b], s, p)
         self.n[b] += count
 
+    def max_rollback(self, b: int) -> int:
+        """How many of the newest tokens can be discarded exactly: the slack (every slot that a
+        discarded token overwrote held a position older than the window that remains); all of them
+        for a contiguous cache (W = 0, nothing is ever overwritten)."""
+        if self.W == 0:
+            return int(self.n[b])
+        return int(min(self.n[b], self.slack))
+
+    def rollback(self, b: int, count: int) -> int:
+        """Discard the newest ``count`` tokens (clamped to [0, max_rollback]): their slots are
+        marked empty and n shrinks. Returns how many were discarded."""
+        d = int(max(0, min(count, self.max_rollback(b))))
+        if d:
+            p = np.arange(self.n[b] - d, self.n[b], dtype=np.int64)
+            self.tags[b, ring_slot(p, self.S, self.Wp)] = -1
+            self.n[b] -= d
+        return d
+
     def occupied_slots(self, b: int) -> np.ndarray:
         return np.nonzero(self.tags[b] >= 0)[0]
+
+    def attended_slots(self, b: int) -> np.ndarray:
+        """Slots holding the positions a windowed draft step attends (sinks + last W)."""
+        n = int(self.n[b])
+        pos = np.concatenate([np.arange(a, c, dtype=np.int64)
+                              for a, c in windowed_positions(n, self.S, self.W)])
+        slots = ring_slot(pos, self.S, self.Wp)
+        if not np.array_equal(self.tags[b, slots], pos):
+            raise AssertionError("ring model lost an attended position")
+        return np.sort(slots)
+
+
+def greedy_accept(target_logits: np.ndarray, draft_tokens: np.ndarray):
+    """Greedy verification of k draft tokens (the standard accept/reject rule under greedy
+    decoding; MASW page, section 1 and 4.3: the target keeps its accept/reject rule and rejected
+    speculative draft KV is discarded).
+
+    ``target_logits`` is ``[B][k+1][V]``: row i scores the token that follows the prefix plus the
+    first i drafts. Draft token i is accepted while it equals the target's choice (argmax; the
+    lowest index on ties) at row i and every earlier draft was accepted. The target's choice at the
+    first rejected row (or at row k when all are accepted) is the next token. Returns
+    ``(choice [B][k+1], n_accept [B], next_token [B], n_drop [B] = k - n_accept)``."""
+    logits = np.asarray(target_logits)
+    B, k1, _ = logits.shape
+    k = k1 - 1
+    draft = np.asarray(draft_tokens).reshape(B, k)
+    choice = np.argmax(logits, axis=2).astype(np.int64)  # first maximum on ties
+    n_accept = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        a = 0
+        while a < k and draft[b, a] == choice[b, a]:
+            a += 1
+        n_accept[b] = a
+    next_token = choice[np.arange(B), n_accept]
+    return choice, n_accept, next_token, k - n_accept
 
 
 # --------------------------------------------------------------------------------------------
@@ -303,16 +370,17 @@ def verify(q, q_dtype, kv: LogicalKV, n: Sequence[int], scale: float, nthreads: 
 
 
 def ring_attention(q, q_dtype, ring_k, ring_v, kv_dtype: int, tags: np.ndarray, scale: float,
-                   nthreads: int = 0):
-    """Attention over the occupied slots of ring buffers ``[B][Hkv][S+W][d]`` as the hardware
-    layout holds them (slots in slot order, whatever positions they carry). ``tags[b, s] >= 0``
-    marks an occupied slot."""
+                   nthreads: int = 0, slots=None):
+    """Attention over slots of ring buffers ``[B][Hkv][slots][d]`` as the hardware layout holds
+    them (slots in slot order, whatever positions they carry): the occupied slots
+    (``tags[b, s] >= 0``), or the slots ``slots[b]`` when given (a ring with slack also holds
+    positions older than the window)."""
     B = q.shape[0]
     nslots = ring_k.shape[2]
     kv = LogicalKV(ring_k, ring_v, kv_dtype, [[(0, 0, nslots)] for _ in range(B)])
     sets = []
     for b in range(B):
-        occ = np.nonzero(tags[b] >= 0)[0]
+        occ = np.nonzero(tags[b] >= 0)[0] if slots is None else np.sort(np.asarray(slots[b]))
         runs: List[Range] = []
         for s in occ:
             if runs and runs[-1][1] == s:
@@ -325,7 +393,7 @@ def ring_attention(q, q_dtype, ring_k, ring_v, kv_dtype: int, tags: np.ndarray, 
 
 def ring_expected(model: RingModel, kv: LogicalKV):
     """Expected ring contents for the positions recorded in ``model.tags``: K and V arrays
-    ``[B][Hkv][S+W][d]`` (rows of empty slots are zero) gathered from the logical sequence."""
+    ``[B][Hkv][slots][d]`` (rows of empty slots are zero) gathered from the logical sequence."""
     B, Hkv, _, d = kv.k.shape
     nslots = model.tags.shape[1]
     rk = np.zeros((B, Hkv, nslots, d), dtype=kv.k.dtype)

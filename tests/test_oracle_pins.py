@@ -433,3 +433,155 @@ def test_dropped_fraction_matches_page_figure():
     for ctx in (1 << 17, 1 << 19, 1 << 20, 1 << 21):
         kept = sum(b - a for a, b in oracle.windowed_positions(ctx, 4, 4096))
         assert kept == 4100
+
+
+# ------------------------------------------------------------------------------------------
+# Ring rollback (MASW page, section 4.3: speculative local KV is discarded after a rejection)
+# ------------------------------------------------------------------------------------------
+def _attended_positions(model, b=0):
+    return sorted(model.tags[b, model.attended_slots(b)].tolist())
+
+
+@pytest.mark.parametrize("S,W,slack", [(4, 8, 3), (0, 5, 5), (1, 1, 2), (3, 16, 4)])
+def test_rollback_returns_to_the_state_without_the_rejected_tokens(S, W, slack):
+    """After any interleaving of appends and rollbacks (each at most `slack` deep), the attended
+    positions are exactly the sinks and the last W of the n present, at their slot-map slots, and
+    they sit where a ring that appended only those n tokens holds them."""
+    rng = np.random.default_rng(S * 100 + W * 10 + slack)
+    model = oracle.RingModel(1, S, W, slack)
+    n = 0
+    for step in range(60):
+        c = int(rng.integers(1, slack + 3))
+        model.append(0, c)
+        n += c
+        d = int(rng.integers(0, c + 1))
+        got = model.rollback(0, d)
+        assert got == min(d, slack, n)
+        n -= got
+        assert model.n[0] == n
+        expect = list(range(min(S, n))) + list(range(max(S, n - W), n))
+        assert _attended_positions(model) == expect
+        fresh = oracle.RingModel(1, S, W, slack)
+        fresh.append(0, n)
+        slots = model.attended_slots(0)
+        assert np.array_equal(slots, fresh.attended_slots(0))
+        assert np.array_equal(model.tags[0, slots], fresh.tags[0, slots])
+        for s in slots:
+            assert oracle.ring_slot(int(model.tags[0, s]), S, W + slack) == s
+
+
+def test_rollback_is_clamped_to_the_slack_and_marks_slots_empty():
+    model = oracle.RingModel(1, 2, 4, 2)
+    model.append(0, 10)
+    before = model.tags.copy()
+    assert model.rollback(0, 5) == 2  # only the slack can be undone exactly
+    assert model.n[0] == 8
+    # slots of positions 8 and 9 are now empty; every other slot is unchanged
+    emptied = [oracle.ring_slot(p, 2, 6) for p in (8, 9)]
+    assert all(model.tags[0, s] == -1 for s in emptied)
+    keep = [s for s in range(8) if s not in emptied]
+    assert np.array_equal(model.tags[0, keep], before[0, keep])
+    assert model.rollback(0, -3) == 0
+    none = oracle.RingModel(1, 2, 4, 0)
+    none.append(0, 10)
+    assert none.rollback(0, 1) == 0  # a compact ring without slack cannot roll back
+    flat = oracle.RingModel(1, 64, 0, 0)  # contiguous cache: nothing is overwritten
+    flat.append(0, 10)
+    assert flat.rollback(0, 7) == 7 and flat.n[0] == 3
+    assert flat.tags[0, :3].tolist() == [0, 1, 2] and (flat.tags[0, 3:] == -1).all()
+
+
+def test_rollback_then_reappend_attends_the_replacement_tokens(oracle_lib):
+    """Speculative loop on real rows: drafts are appended, some rejected and replaced by other
+    tokens at the same positions. Attention over the ring's attended slots equals windowed
+    attention over the final logical sequence (the rows each position ends up holding)."""
+    S, W, slack, Hkv, Hq, d = 3, 7, 4, 2, 4, 8
+    rng = np.random.default_rng(7)
+    model = oracle.RingModel(1, S, W, slack)
+    nslots = S + W + slack
+    ring_k = np.zeros((1, Hkv, nslots, d))
+    ring_v = np.zeros((1, Hkv, nslots, d))
+    seq_k, seq_v = [], []  # final content of every position, as lists of [Hkv][d] rows
+
+    def write(rows_k, rows_v):
+        for rk, rv in zip(rows_k, rows_v):
+            p = int(model.n[0])
+            s = oracle.ring_slot(p, S, W + slack)
+            ring_k[0, :, s], ring_v[0, :, s] = rk, rv
+            model.append(0, 1)
+            if p < len(seq_k):
+                seq_k[p], seq_v[p] = rk, rv
+            else:
+                seq_k.append(rk)
+                seq_v.append(rv)
+
+    write(rng.standard_normal((20, Hkv, d)), rng.standard_normal((20, Hkv, d)))
+    for step in range(12):
+        k = int(rng.integers(1, slack + 1))
+        write(rng.standard_normal((k, Hkv, d)), rng.standard_normal((k, Hkv, d)))
+        drop = model.rollback(0, int(rng.integers(0, k + 1)))
+        del seq_k[len(seq_k) - drop:], seq_v[len(seq_v) - drop:]
+        write(rng.standard_normal((1, Hkv, d)), rng.standard_normal((1, Hkv, d)))  # correction
+        n = int(model.n[0])
+        assert n == len(seq_k)
+        q = rng.standard_normal((1, 1, Hq, d))
+        lk = np.stack(seq_k, axis=1)[None]
+        lv = np.stack(seq_v, axis=1)[None]
+        o_seq, l_seq = oracle.draft_windowed(q, F64, oracle.contiguous_kv(lk, lv, F64), [n], S,
+                                             W, 0.4)
+        o_ring, l_ring = oracle.ring_attention(q, F64, ring_k, ring_v, F64, model.tags, 0.4,
+                                               slots=[model.attended_slots(0)])
+        np.testing.assert_allclose(o_ring, o_seq, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(l_ring, l_seq, rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------------------------------------
+# Greedy accept/reject (the target's standard rule under greedy decoding)
+# ------------------------------------------------------------------------------------------
+def test_greedy_accept_hand_cases():
+    V = 6
+    logits = np.full((3, 4, V), -1.0)
+    choice = [[2, 5, 1, 0], [2, 5, 1, 0], [3, 3, 3, 4]]
+    for b in range(3):
+        for i in range(4):
+            logits[b, i, choice[b][i]] = 2.0
+    draft = np.array([[2, 5, 1], [2, 4, 1], [0, 3, 3]])
+    ch, n_acc, nxt, drop = oracle.greedy_accept(logits, draft)
+    assert ch.tolist() == choice
+    assert n_acc.tolist() == [3, 1, 0]  # all kept; second rejected; first rejected
+    assert nxt.tolist() == [0, 5, 3]  # bonus token; correction at row 1; correction at row 0
+    assert drop.tolist() == [0, 2, 3]
+
+
+def test_greedy_accept_ties_take_the_lowest_index():
+    logits = np.zeros((1, 2, 5))
+    logits[0, 0, [1, 3]] = 7.0
+    logits[0, 1, [4, 0]] = 7.0
+    ch, n_acc, nxt, _ = oracle.greedy_accept(logits, np.array([[3]]))
+    assert ch.tolist() == [[1, 0]]
+    assert n_acc.tolist() == [0] and nxt.tolist() == [1]
+    ch, n_acc, nxt, _ = oracle.greedy_accept(logits, np.array([[1]]))
+    assert n_acc.tolist() == [1] and nxt.tolist() == [0]
+
+
+def test_greedy_accept_matches_plain_loops():
+    """Brute force with Python loops and comparisons (no argmax routine)."""
+    rng = np.random.default_rng(11)
+    B, k, V = 5, 4, 9
+    for trial in range(30):
+        logits = rng.integers(-3, 4, size=(B, k + 1, V)).astype(np.float64)  # many ties
+        draft = rng.integers(0, V, size=(B, k))
+        ch, n_acc, nxt, drop = oracle.greedy_accept(logits, draft)
+        for b in range(B):
+            picks = []
+            for i in range(k + 1):
+                best = 0
+                for t in range(1, V):
+                    if logits[b, i, t] > logits[b, i, best]:
+                        best = t
+                picks.append(best)
+            a = 0
+            while a < k and draft[b, a] == picks[a]:
+                a += 1
+            assert ch[b].tolist() == picks
+            assert n_acc[b] == a and nxt[b] == picks[a] and drop[b] == k - a

@@ -63,10 +63,15 @@ def lib():
         L.wmtp_attn_workspace_bytes.restype = sz
         L.wmtp_status_string.argtypes = [ctypes.c_int]
         L.wmtp_status_string.restype = ctypes.c_char_p
+        L.wmtp_ring_rollback.argtypes = [kvp, vp, vp]
+        L.wmtp_greedy_accept.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.wmtp_accept_workspace_bytes.argtypes = [i32, i32, i32]
+        L.wmtp_accept_workspace_bytes.restype = sz
         L.wmtp_probe_read.argtypes = [vp, sz, vp, vp]
         L.wmtp_llc_flush.argtypes = [vp, sz, ctypes.c_uint8, vp]
         for name in ("wmtp_ring_append", "wmtp_draft_attn_windowed", "wmtp_draft_attn_full",
-                     "wmtp_verify_attn", "wmtp_probe_read", "wmtp_llc_flush"):
+                     "wmtp_verify_attn", "wmtp_ring_rollback", "wmtp_greedy_accept",
+                     "wmtp_probe_read", "wmtp_llc_flush"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -129,7 +134,7 @@ class KVCache:
     def allocate(cls, batch, n_kv_heads, head_dim, capacity, sink, window, torch_dtype,
                  device="cuda", with_pos=True):
         """Zeroed cache tensors (torch owns the memory). Ring: window >= 1 and
-        capacity = sink + window; contiguous: window = 0 and sink = capacity."""
+        capacity >= sink + window; contiguous: window = 0 and sink = capacity."""
         import torch
 
         shape = (batch, n_kv_heads, capacity, head_dim)
@@ -143,8 +148,10 @@ class KVCache:
 
     @classmethod
     def ring(cls, batch, n_kv_heads, head_dim, sink, window, torch_dtype, device="cuda",
-             with_pos=True):
-        return cls.allocate(batch, n_kv_heads, head_dim, sink + window, sink, window,
+             with_pos=True, slack=0):
+        """A ring of sink + window + slack slots (slack > 0 allows rolling back that many of the
+        newest tokens)."""
+        return cls.allocate(batch, n_kv_heads, head_dim, sink + window + slack, sink, window,
                             torch_dtype, device, with_pos)
 
     @classmethod
@@ -269,6 +276,52 @@ def wmtp_llc_flush(buf, value: int = 0, stream=None, check=True) -> int:
     n = buf.numel() * buf.element_size()
     st = lib().wmtp_llc_flush(_ptr(buf), int(n), int(value) & 0xFF, _stream(stream))
     return _done(st, "wmtp_llc_flush", check)
+
+
+def wmtp_ring_rollback(cache, n_drop, stream=None, check=True) -> int:
+    """Discard the newest n_drop[b] tokens of every sequence (device int32 [batch])."""
+    d = _desc(cache)
+    _numel_ok(n_drop, d.batch, 4, "n_drop")
+    st = lib().wmtp_ring_rollback(ctypes.byref(d), _ptr(n_drop), _stream(stream))
+    return _done(st, "wmtp_ring_rollback", check)
+
+
+def wmtp_accept_workspace_bytes(batch: int, k: int, vocab: int) -> int:
+    return int(lib().wmtp_accept_workspace_bytes(batch, k, vocab))
+
+
+def wmtp_greedy_accept(logits, k: int, draft_tokens, choice, n_accept, next_token, n_drop, ws,
+                       ws_bytes: Optional[int] = None, stream=None, check=True) -> int:
+    """Greedy verification: logits [B][k+1][V] (float32 or bfloat16), draft_tokens [B][k] int32;
+    writes choice [B][k+1], n_accept, next_token and n_drop [B] (int32)."""
+    B, k1, V = (int(x) for x in logits.shape)
+    if k1 != k + 1:
+        raise ValueError("logits must hold k + 1 rows per sequence")
+    code = dtype_code(logits.dtype)
+    _numel_ok(logits, B * k1 * V, 2 if code == WMTP_BF16 else 4, "logits")
+    if k > 0:
+        _numel_ok(draft_tokens, B * k, 4, "draft_tokens")
+    _numel_ok(choice, B * k1, 4, "choice")
+    for t, name in ((n_accept, "n_accept"), (next_token, "next_token"), (n_drop, "n_drop")):
+        _numel_ok(t, B, 4, name)
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    st = lib().wmtp_greedy_accept(_ptr(logits), code, B, int(k), V,
+                                  _ptr(draft_tokens) if k > 0 else None, _ptr(choice),
+                                  _ptr(n_accept), _ptr(next_token), _ptr(n_drop), _ptr(ws),
+                                  int(nbytes), _stream(stream))
+    return _done(st, "wmtp_greedy_accept", check)
+
+
+def accept_workspace(batch: int, k: int, vocab: int, device="cuda"):
+    """A 256-byte-aligned device byte tensor large enough for wmtp_greedy_accept."""
+    import torch
+
+    n = wmtp_accept_workspace_bytes(batch, k, vocab)
+    if n == 0:
+        raise ValueError("wmtp_greedy_accept does not accept these sizes")
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]
 
 
 def wmtp_attn_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, m: int,

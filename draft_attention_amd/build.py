@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libwmtp.so")
-SOURCES = ["abi.hip", "attn.hip", "ring.hip", "probe.hip"]
+SOURCES = ["abi.hip", "attn.hip", "ring.hip", "accept.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

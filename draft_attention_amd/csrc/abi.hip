@@ -12,6 +12,7 @@ namespace {
 using wmtp::SplitPlan;
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxAcceptK = 63;  // draft tokens per greedy verification
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -33,7 +34,8 @@ int check_kv(const wmtp_kv* c) {
   if (c->capacity > wmtp::kMaxCapacity) return WMTP_ERR_CAPACITY;
   if (c->sink < 0 || c->window < 0) return WMTP_ERR_INVALID_ARG;
   if (c->window >= 1) {
-    if ((long long)c->sink + c->window != c->capacity) return WMTP_ERR_INVALID_ARG;
+    // a ring: S sinks, W attended window slots and capacity - S - W >= 0 slack slots
+    if ((long long)c->sink + c->window > c->capacity) return WMTP_ERR_INVALID_ARG;
   } else if (c->sink != c->capacity) {
     return WMTP_ERR_INVALID_ARG;
   }
@@ -74,6 +76,9 @@ int attention_call(const wmtp_kv* c, const void* q, int m, int n_q_heads, float 
   a.limit = limit;
   a.mode = mode;
   a.sm_scale = sm_scale;
+  a.sink = c->sink;
+  a.window = c->window;
+  a.wphys = c->window >= 1 ? c->capacity - c->sink : 0;
   hipError_t e = wmtp::launch_attention(a, plan, c->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WMTP_OK : WMTP_ERR_HIP;
 }
@@ -102,7 +107,7 @@ int wmtp_ring_append(const wmtp_kv* cache, const void* k_new, const void* v_new,
   a.head_dim = cache->head_dim;
   a.capacity = cache->capacity;
   a.sink = cache->sink;
-  a.window = cache->window;
+  a.window = cache->window == 0 ? 0 : cache->capacity - cache->sink;  // physical window
   a.n_new = n_new;
   a.elem_bytes = elem_bytes(cache->dtype);
   hipError_t e = wmtp::launch_append(a, static_cast<hipStream_t>(stream));
@@ -139,6 +144,64 @@ int wmtp_verify_attn(const wmtp_kv* cache, const void* q, int32_t m, int32_t n_q
   if (max_seq_len < 1 || max_seq_len > cache->capacity) return WMTP_ERR_INVALID_ARG;
   return attention_call(cache, q, m, n_q_heads, sm_scale, max_seq_len, wmtp::kModeVerify, out, lse,
                         ws, ws_bytes, stream);
+}
+
+int wmtp_ring_rollback(const wmtp_kv* cache, const int32_t* n_drop, void* stream) {
+  int st = check_kv(cache);
+  if (st != WMTP_OK) return st;
+  if (!n_drop || !aligned(n_drop, 4)) return WMTP_ERR_INVALID_ARG;
+  wmtp::RollbackArgs a;
+  a.pos = cache->pos;
+  a.seq_len = cache->seq_len;
+  a.n_drop = n_drop;
+  a.batch = cache->batch;
+  a.capacity = cache->capacity;
+  a.sink = cache->sink;
+  a.window = cache->window == 0 ? 0 : cache->capacity - cache->sink;
+  a.slack = cache->window == 0 ? 0 : cache->capacity - cache->sink - cache->window;
+  hipError_t e = wmtp::launch_rollback(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WMTP_OK : WMTP_ERR_HIP;
+}
+
+size_t wmtp_accept_workspace_bytes(int32_t batch, int32_t k, int32_t vocab) {
+  if (batch < 1 || k < 0 || k > kMaxAcceptK || vocab < 1) return 0;
+  const size_t chunks = ((size_t)vocab + wmtp::kAcceptChunk - 1) / wmtp::kAcceptChunk;
+  const size_t entries = (size_t)batch * (k + 1) * chunks;
+  return round_up(entries * sizeof(float), kAlign) + entries * sizeof(int32_t);
+}
+
+int wmtp_greedy_accept(const void* logits, int32_t dtype, int32_t batch, int32_t k, int32_t vocab,
+                       const int32_t* draft_tokens, int32_t* choice, int32_t* n_accept,
+                       int32_t* next_token, int32_t* n_drop, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (dtype != WMTP_F32 && dtype != WMTP_BF16) return WMTP_ERR_UNSUPPORTED;
+  if (batch < 1 || k < 0 || k > kMaxAcceptK || vocab < 1) return WMTP_ERR_INVALID_ARG;
+  if ((size_t)batch * (k + 1) > 65535) return WMTP_ERR_INVALID_ARG;  // one grid row each
+  if (!logits || !aligned(logits, elem_bytes(dtype))) return WMTP_ERR_INVALID_ARG;
+  if (k > 0 && (!draft_tokens || !aligned(draft_tokens, 4))) return WMTP_ERR_INVALID_ARG;
+  if (!choice || !n_accept || !next_token || !n_drop) return WMTP_ERR_INVALID_ARG;
+  if (!aligned(choice, 4) || !aligned(n_accept, 4) || !aligned(next_token, 4) || !aligned(n_drop, 4))
+    return WMTP_ERR_INVALID_ARG;
+  const size_t need = wmtp_accept_workspace_bytes(batch, k, vocab);
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return WMTP_ERR_WORKSPACE;
+  wmtp::AcceptArgs a;
+  a.logits = logits;
+  a.draft = draft_tokens;
+  a.choice = choice;
+  a.n_accept = n_accept;
+  a.next_token = next_token;
+  a.n_drop = n_drop;
+  a.batch = batch;
+  a.k = k;
+  a.vocab = vocab;
+  a.chunks = (vocab + wmtp::kAcceptChunk - 1) / wmtp::kAcceptChunk;
+  a.dtype = dtype;
+  const size_t entries = (size_t)batch * (k + 1) * a.chunks;
+  a.ws_val = static_cast<float*>(ws);
+  a.ws_idx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                        round_up(entries * sizeof(float), kAlign));
+  hipError_t e = wmtp::launch_accept(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WMTP_OK : WMTP_ERR_HIP;
 }
 
 size_t wmtp_attn_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,

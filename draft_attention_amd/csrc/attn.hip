@@ -147,10 +147,45 @@ struct RowState {
   f32x4_t o[NR][Frag<D, BF16>::kBlocks];
 };
 
-template <int D, int NR, bool BF16>
+// Windowed read of a ring with slack (capacity = S + W + slack): every slot is scanned and a slot
+// is attended iff it holds a sink (slot s < min(S, n)) or one of the last W positions. The window
+// slots hold positions in wrap order, so the age of window slot S + u (0 = newest position) is
+// (top - u) mod Wp with top = (n - 1 - S) mod Wp, Wp = W + slack, and the slot is attended iff its
+// age < min(W, n - S). The test depends on n alone, so loads never wait for it.
+struct RingMask {
+  bool active;
+  int n, sink, wphys, top, wcount;
+  __device__ __forceinline__ bool attended(int s) const {
+    if (s < sink) return s < n;
+    int age = top - (s - sink);
+    age += age < 0 ? wphys : 0;
+    return age < wcount;
+  }
+};
+
+// A windowed read of a ring with slack slots (kernels instantiated with RING = true).
+inline bool ring_masked(const AttnArgs& a) { return a.mode == kModeWindowed && a.wphys > a.window; }
+
+__device__ __forceinline__ RingMask ring_mask(const AttnArgs& a, int raw_n) {
+  RingMask r;
+  r.active = a.mode == kModeWindowed && a.wphys > a.window;
+  r.n = raw_n;
+  r.sink = a.sink;
+  r.wphys = a.wphys > 0 ? a.wphys : 1;
+  r.top = 0;
+  r.wcount = 0;
+  if (r.active && raw_n > a.sink) {  // the modulo only for rings with slack
+    r.top = (raw_n - 1 - a.sink) % r.wphys;
+    r.wcount = min(a.window, raw_n - a.sink);
+  }
+  return r;
+}
+
+template <int D, int NR, bool BF16, bool RING>
 __device__ __forceinline__ void compute_tile(const Tile<D, BF16>& T, const QOperand<D, NR, BF16>& qf,
                                              int t0, int last, const int (&last_visible)[NR],
-                                             int grp, float scale_log2, RowState<D, NR, BF16>& st) {
+                                             const RingMask& rm, int grp, float scale_log2,
+                                             RowState<D, NR, BF16>& st) {
   using F = Frag<D, BF16>;
   // ---------------- S^T = K_tile . Q^T
   f32x4_t s[NR];
@@ -189,6 +224,11 @@ __device__ __forceinline__ void compute_tile(const Tile<D, BF16>& T, const QOper
   float sc[NR][4];
   bool need = false;
   float mx[NR];
+  bool ring_ok[4] = {true, true, true, true};
+  if constexpr (RING) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ring_ok[j] = rm.attended(t0 + 4 * grp + j);
+  }
 #pragma unroll
   for (int rb = 0; rb < NR; ++rb) {
     const int vis = min(last, last_visible[rb]);
@@ -196,7 +236,7 @@ __device__ __forceinline__ void compute_tile(const Tile<D, BF16>& T, const QOper
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = t0 + 4 * grp + j;
-      sc[rb][j] = (key <= vis) ? s[rb][j] * scale_log2 : -INFINITY;
+      sc[rb][j] = (key <= vis && ring_ok[j]) ? s[rb][j] * scale_log2 : -INFINITY;
       m = fmaxf(m, sc[rb][j]);
     }
     mx[rb] = m;
@@ -298,7 +338,7 @@ constexpr bool pipelined() {
   return q + o + 2 * tile <= 224 && o <= 96;
 }
 
-template <int D, int NR, bool BF16>
+template <int D, int NR, bool BF16, bool RING>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_splits,
                                                               int n_chunks, int chunk_rows) {
   using F = Frag<D, BF16>;
@@ -322,6 +362,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
 
   int n = a.seq_len[b];
   n = max(n, 0);
+  const RingMask rm = ring_mask(a, n);
   n = min(n, a.limit);
   const int last = n - 1;
 
@@ -392,18 +433,18 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
     // software-pipelined tile loop: two register tiles, the next one always in flight
     while (t < n) {
       load_tile<D, BF16>(kbase, vbase, t + kStride, last, r16, grp, B);
-      compute_tile<D, NR, BF16>(A, qf, t, last, last_visible, grp, scale_log2, st);
+      compute_tile<D, NR, BF16, RING>(A, qf, t, last, last_visible, rm, grp, scale_log2, st);
       t += kStride;
       if (t >= n) break;
       load_tile<D, BF16>(kbase, vbase, t + kStride, last, r16, grp, A);
-      compute_tile<D, NR, BF16>(B, qf, t, last, last_visible, grp, scale_log2, st);
+      compute_tile<D, NR, BF16, RING>(B, qf, t, last, last_visible, rm, grp, scale_log2, st);
       t += kStride;
     }
   } else {
     // one register tile: loads of tile t + stride start once tile t is consumed
     (void)B;
     while (t < n) {
-      compute_tile<D, NR, BF16>(A, qf, t, last, last_visible, grp, scale_log2, st);
+      compute_tile<D, NR, BF16, RING>(A, qf, t, last, last_visible, rm, grp, scale_log2, st);
       t += kStride;
       if (t < n) load_tile<D, BF16>(kbase, vbase, t, last, r16, grp, A);
     }
@@ -536,7 +577,7 @@ __device__ __forceinline__ int coop_slot(int key, int chunk, int tensor) {
   return key * C::kRowBytes + (chunk << 4);
 }
 
-template <int D, int NB, bool BF16>
+template <int D, int NB, bool BF16, bool RING>
 #ifndef WMTP_COOP_WPC
 #define WMTP_COOP_WPC 2
 #endif
@@ -564,6 +605,7 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
 
   int n = a.seq_len[b];
   n = max(n, 0);
+  const RingMask rm = ring_mask(a, n);
   n = min(n, a.limit);
   const int last = n - 1;
   const int tiles = (n + kTileKeys - 1) / kTileKeys;
@@ -674,7 +716,7 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
     const int vis = live ? min(last, last_visible) : -1;
     float sc[4];
     float mx = -INFINITY;
-    if (live && t0 + kTileKeys - 1 <= vis_all) {  // workgroup-uniform: no key of the tile masked
+    if (!RING && live && t0 + kTileKeys - 1 <= vis_all) {  // workgroup-uniform: none masked
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         sc[j] = sacc[j] * scale_log2;
@@ -684,7 +726,8 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int key = t0 + 4 * grp + j;
-        sc[j] = (key <= vis) ? sacc[j] * scale_log2 : -INFINITY;
+        const bool ok = key <= vis && (!RING || rm.attended(key));
+        sc[j] = ok ? sacc[j] * scale_log2 : -INFINITY;
         mx = fmaxf(mx, sc[j]);
       }
     }
@@ -907,11 +950,17 @@ hipError_t launch_split(const AttnArgs& a, const SplitPlan& p, hipStream_t strea
   // row blocks beyond the register budget of (D, dtype) are never planned (rows_cap)
   constexpr int kMaxNr = BF16 ? (D == 256 ? 2 : 4) : (D == 64 ? 4 : (D == 128 ? 2 : 1));
   if (p.nr < 1 || p.nr > kMaxNr) return hipErrorInvalidValue;
-  switch (p.nr) {
-    case 1: attn_split_kernel<D, 1, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
-    case 2: if constexpr (kMaxNr >= 2) attn_split_kernel<D, 2, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
-    case 3: if constexpr (kMaxNr >= 3) attn_split_kernel<D, 3, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
-    default: if constexpr (kMaxNr >= 4) attn_split_kernel<D, 4, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+  if (ring_masked(a)) {
+    // a windowed draft step has one query token: G <= 16 rows, one row block
+    if (p.nr != 1) return hipErrorInvalidValue;
+    attn_split_kernel<D, 1, BF16, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
+  } else {
+    switch (p.nr) {
+      case 1: attn_split_kernel<D, 1, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+      case 2: if constexpr (kMaxNr >= 2) attn_split_kernel<D, 2, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+      case 3: if constexpr (kMaxNr >= 3) attn_split_kernel<D, 3, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+      default: if constexpr (kMaxNr >= 4) attn_split_kernel<D, 4, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -924,10 +973,24 @@ template <int D, bool BF16>
 hipError_t launch_coop(const AttnArgs& a, const SplitPlan& p, hipStream_t stream) {
   dim3 grid(p.n_splits, a.batch * a.n_kv_heads * p.n_chunks);
   dim3 block(kThreads);
+  const bool ring = ring_masked(a);
   switch (p.nr) {
-    case 1: if constexpr (!(BF16 && D == 64)) attn_coop_kernel<D, 1, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
-    case 2: attn_coop_kernel<D, 2, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
-    case 4: if constexpr (BF16 || D != 256) attn_coop_kernel<D, 4, BF16><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+    case 1:
+      if constexpr (!(BF16 && D == 64)) {
+        if (ring) attn_coop_kernel<D, 1, BF16, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
+        else attn_coop_kernel<D, 1, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
+      }
+      break;
+    case 2:
+      if (ring) attn_coop_kernel<D, 2, BF16, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
+      else attn_coop_kernel<D, 2, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
+      break;
+    case 4:
+      if constexpr (BF16 || D != 256) {
+        if (ring) attn_coop_kernel<D, 4, BF16, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
+        else attn_coop_kernel<D, 4, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
+      }
+      break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

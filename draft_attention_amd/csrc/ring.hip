@@ -10,6 +10,11 @@
 // (p >= n + n_new - W); any other token would be overwritten within the same append. So a bulk
 // append never writes one slot twice, and the workgroups of a launch never race on a slot.
 //
+// A ring may carry slack window slots beyond the W the draft attends (capacity = S + W + slack):
+// appends then wrap over W + slack slots (the `window` these kernels receive is that physical
+// window), and the newest `slack` tokens can be discarded again exactly (rollback_kernel): every
+// slot they overwrote held a position older than the W-token window that remains.
+//
 // seq_len[b] is read by every thread that computes slots and advanced by n_new. When one workgroup
 // handles a whole sequence it advances seq_len itself after a barrier (one launch); when a bulk
 // append is spread over many workgroups, a second one-wavefront kernel advances it after the copy.
@@ -109,7 +114,32 @@ __global__ __launch_bounds__(64) void append_bump_kernel(int32_t* seq_len, int b
   }
 }
 
+// Discard the newest n_drop[b] tokens of sequence b (clamped to [0, max_drop(n)]): the tags of
+// their slots become -1 and seq_len[b] shrinks. One workgroup per sequence; every thread reads seq_len[b]
+// before thread 0 changes it.
+__global__ __launch_bounds__(64) void rollback_kernel(RollbackArgs a) {
+  const int b = blockIdx.x;
+  const int64_t n = present(a.seq_len, b);
+  int64_t d = a.n_drop[b];
+  const int64_t cap = a.window == 0 ? n : (n < a.slack ? n : (int64_t)a.slack);
+  d = d < 0 ? 0 : (d > cap ? cap : d);
+  if (a.pos) {
+    for (int64_t i = threadIdx.x; i < d; i += blockDim.x) {
+      const int64_t p = n - d + i;
+      const int64_t slot = slot_of(p, a.sink, a.window);
+      if (slot < a.capacity) a.pos[(size_t)b * a.capacity + slot] = -1;  // contiguous: p may pass it
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.seq_len[b] = (int32_t)(n - d);
+}
+
 }  // namespace
+
+hipError_t launch_rollback(const RollbackArgs& a, hipStream_t stream) {
+  rollback_kernel<<<dim3(a.batch), dim3(64), 0, stream>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   // host-side bound on the survivors of any sequence

@@ -62,6 +62,10 @@ struct AttnArgs {
   int limit;  // keys beyond min(seq_len, limit) are never read
   int mode;
   float sm_scale;
+  // windowed mode on a ring with slack (wphys > window): key i of the attended set lives in slot
+  // i for the min(S, n) sinks, else in slot S + (w0 - S + i - sinks) mod wphys with
+  // w0 = max(sinks, n - window). With wphys == window the attended keys are slots 0..limit-1.
+  int sink, window, wphys;
 };
 
 hipError_t launch_attention(const AttnArgs& a, const SplitPlan& p, int dtype, hipStream_t stream);
@@ -76,6 +80,33 @@ struct AppendArgs {
   int batch, n_kv_heads, head_dim, capacity, sink, window, n_new, elem_bytes;
 };
 
+// `window` is the physical window of a ring (capacity - sink; 0 for a contiguous cache).
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
+struct RollbackArgs {
+  int32_t* pos;
+  int32_t* seq_len;
+  const int32_t* n_drop;
+  int batch, capacity, sink;
+  int window;  // physical window (capacity - sink) of a ring, 0 for a contiguous cache
+  int slack;   // ring: tokens that can be discarded exactly (capacity - sink - attended window)
+};
+
+hipError_t launch_rollback(const RollbackArgs& a, hipStream_t stream);
+
+struct AcceptArgs {
+  const void* logits;  // [batch][k+1][vocab]
+  const int32_t* draft;  // [batch][k]
+  int32_t* choice;       // [batch][k+1]
+  int32_t* n_accept;     // [batch]
+  int32_t* next_token;   // [batch]
+  int32_t* n_drop;       // [batch]
+  float* ws_val;         // [batch*(k+1)][chunks]
+  int32_t* ws_idx;       // [batch*(k+1)][chunks]
+  int batch, k, vocab, chunks, dtype;
+};
+
+constexpr int kAcceptChunk = 4096;  // vocabulary entries per argmax workgroup
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
 
 }  // namespace wmtp

@@ -69,9 +69,15 @@ typedef enum wmtp_status {
 
 typedef enum wmtp_dtype { WMTP_F32 = 0, WMTP_BF16 = 1 } wmtp_dtype;
 
-/* A KV cache of `batch` sequences: a compact ring buffer (window >= 1, capacity = sink + window) or
+/* A KV cache of `batch` sequences: a compact ring buffer (window >= 1, capacity >= sink + window) or
  * a contiguous cache (window = 0, sink = capacity). head_dim must be 64, 128 or 256;
- * 1 <= capacity <= 2^30 (larger capacities return WMTP_ERR_CAPACITY). */
+ * 1 <= capacity <= 2^30 (larger capacities return WMTP_ERR_CAPACITY).
+ * A ring's window positions wrap over its capacity - sink window slots: slot(p) = p for p < sink,
+ * else sink + (p - sink) % (capacity - sink). The draft attends the sinks and the last `window`
+ * positions; the slack = capacity - sink - window extra slots let the newest `slack` tokens be
+ * discarded again exactly (wmtp_ring_rollback), since every slot they overwrote held a position
+ * older than the window that remains. slack = 0 is the compact ring of the Windowed-MTP abstract
+ * (last sentence). */
 typedef struct wmtp_kv {
   void* k;          /* device [batch][n_kv_heads][capacity][head_dim] */
   void* v;          /* device [batch][n_kv_heads][capacity][head_dim] */
@@ -90,8 +96,8 @@ typedef struct wmtp_kv {
  * seq_len[b] .. seq_len[b] + n_new - 1), then seq_len[b] += n_new, all on `stream`.
  * For each token, K and V of every KV head are copied bit for bit into slot(p), and pos[b][slot]
  * is set to p when pos is not NULL. In a ring, only the tokens that are still held after the
- * append are written (sinks, and the last `window` positions), so a bulk append of any size writes
- * each slot at most once. In a contiguous cache, tokens whose position would reach `capacity` are
+ * append are written (sinks, and the last capacity - sink positions), so a bulk append of any size
+ * writes each slot at most once. In a contiguous cache, tokens whose position would reach `capacity` are
  * not written (seq_len still advances; the caller's contract is seq_len[b] + n_new <= capacity,
  * which the device cannot report).
  * Errors: INVALID_ARG (null pointers, n_new < 0, bad descriptor), UNSUPPORTED (dtype, head_dim),
@@ -99,10 +105,11 @@ typedef struct wmtp_kv {
 int wmtp_ring_append(const wmtp_kv* cache, const void* k_new, const void* v_new, int32_t n_new,
                      void* stream);
 
-/* Windowed-MTP draft step: one query token per sequence (q is [batch][1][n_q_heads][head_dim])
- * attends the occupied slots of its ring, which hold exactly the sink positions and the last
- * `window` positions: c_b = min(seq_len[b], capacity) slots, 0..c_b-1. `ring` must be a ring
- * (window >= 1). out is [batch][1][n_q_heads][head_dim] float32; lse (nullable) [batch][1][n_q_heads].
+/* Windowed-MTP draft step (abstract, fifth sentence): one query token per sequence (q is
+ * [batch][1][n_q_heads][head_dim]) attends its ring's sink positions {p < sink} and the last
+ * `window` positions {n_b - window <= p < n_b}, each once, n_b = seq_len[b]. Without slack these are
+ * exactly the occupied slots 0..min(n_b, capacity)-1; with slack, the slots holding older positions
+ * are skipped. `ring` must be a ring (window >= 1). out is [batch][1][n_q_heads][head_dim] float32; lse (nullable) [batch][1][n_q_heads].
  * A sequence with seq_len[b] <= 0 gets out = 0 and lse = -inf.
  * ws: device workspace of at least
  *   wmtp_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, 1, capacity) bytes.
@@ -130,6 +137,37 @@ int wmtp_draft_attn_full(const wmtp_kv* cache, const void* q, int32_t n_q_heads,
 int wmtp_verify_attn(const wmtp_kv* cache, const void* q, int32_t m, int32_t n_q_heads,
                      float sm_scale, int32_t max_seq_len, float* out, float* lse, void* ws,
                      size_t ws_bytes, void* stream);
+
+/* Discard the newest n_drop[b] tokens of every sequence b after a rejected speculation (the MASW
+ * page, section 4.3: rejected speculative local KV is discarded). n_drop is device memory [batch],
+ * typically written by wmtp_greedy_accept on the same stream. The count is clamped on the device
+ * to [0, min(seq_len[b], slack)] for a ring and to [0, seq_len[b]] for a contiguous cache (a
+ * contiguous cache overwrites nothing). The slots of the discarded positions get pos = -1 (when
+ * pos is not NULL; positions at or past a contiguous cache's capacity have no slot), then
+ * seq_len[b] shrinks by the count. K/V bytes are left as they are (no call reads them until a
+ * later append overwrites them). Errors: INVALID_ARG (null or misaligned n_drop, bad descriptor),
+ * UNSUPPORTED, HIP. */
+int wmtp_ring_rollback(const wmtp_kv* cache, const int32_t* n_drop, void* stream);
+
+/* Greedy verification of k draft tokens per sequence from the target's logits (the target's
+ * standard accept/reject rule under greedy decoding; MASW page, sections 1 and 4.3).
+ *   logits       device [batch][k+1][vocab], dtype WMTP_F32 or WMTP_BF16 (element-aligned): row i
+ *                scores the token after the prefix and the first i drafts. No NaN entries.
+ *   draft_tokens device int32 [batch][k] (may be NULL when k = 0)
+ *   choice       device int32 [batch][k+1]: argmax of every row (the lowest index on ties)
+ *   n_accept     device int32 [batch]: a = the number of leading drafts equal to choice[b][i]
+ *   next_token   device int32 [batch]: choice[b][a] (the correction, or the bonus token if a = k)
+ *   n_drop       device int32 [batch]: k - a (the draft tokens a rollback should discard)
+ * 0 <= k <= 63, batch*(k+1) <= 65535, vocab >= 1. ws: device, 256-byte aligned, at least
+ * wmtp_accept_workspace_bytes(batch, k, vocab) bytes. Errors: INVALID_ARG, UNSUPPORTED (dtype),
+ * WORKSPACE, HIP. */
+int wmtp_greedy_accept(const void* logits, int32_t dtype, int32_t batch, int32_t k, int32_t vocab,
+                       const int32_t* draft_tokens, int32_t* choice, int32_t* n_accept,
+                       int32_t* next_token, int32_t* n_drop, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Workspace bytes of wmtp_greedy_accept (per-chunk maxima); 0 for arguments it rejects. */
+size_t wmtp_accept_workspace_bytes(int32_t batch, int32_t k, int32_t vocab);
 
 /* Workspace bytes an attention call with these sizes needs (split-K partial results). Pass
  * m = 1 for draft steps and max_seq_len = capacity for the windowed call. Depends only on its

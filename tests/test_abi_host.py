@@ -31,7 +31,8 @@ def test_exports_every_declared_function(lib):
     names = W.header_functions()
     assert set(names) == {"wmtp_ring_append", "wmtp_draft_attn_windowed", "wmtp_draft_attn_full",
                           "wmtp_verify_attn", "wmtp_attn_workspace_bytes", "wmtp_status_string",
-                          "wmtp_probe_read", "wmtp_llc_flush"}
+                          "wmtp_probe_read", "wmtp_llc_flush", "wmtp_ring_rollback",
+                          "wmtp_greedy_accept", "wmtp_accept_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -73,7 +74,7 @@ CONTIG = dict(capacity=64, sink=64, window=0)
     (dict(seq_len=None), W.WMTP_ERR_INVALID_ARG),
     (dict(batch=0), W.WMTP_ERR_INVALID_ARG),
     (dict(n_kv_heads=0), W.WMTP_ERR_INVALID_ARG),
-    (dict(capacity=21), W.WMTP_ERR_INVALID_ARG),          # ring: capacity != sink + window
+    (dict(capacity=19), W.WMTP_ERR_INVALID_ARG),          # ring: capacity < sink + window
     (dict(sink=-1, capacity=15), W.WMTP_ERR_INVALID_ARG),
     (dict(capacity=64, sink=60, window=0), W.WMTP_ERR_INVALID_ARG),  # contiguous: sink != cap
     (dict(k=FAKE + 8), W.WMTP_ERR_INVALID_ARG),           # misaligned
@@ -145,3 +146,44 @@ def test_probe_arguments_rejected_before_launch(lib):
     assert lib.wmtp_llc_flush(None, 1024, 0, None) == W.WMTP_ERR_INVALID_ARG
     assert lib.wmtp_llc_flush(FAKE, 24, 0, None) == W.WMTP_ERR_INVALID_ARG
     assert lib.wmtp_llc_flush(FAKE + 4, 1024, 0, None) == W.WMTP_ERR_INVALID_ARG
+
+
+def test_ring_with_slack_is_a_valid_descriptor_and_short_capacity_is_not(lib):
+    # capacity below sink + window is rejected before anything runs (a NULL k_new fails later)
+    assert _append(_kv(capacity=19)) == W.WMTP_ERR_INVALID_ARG
+    assert _append(_kv(capacity=24), k_new=None) == W.WMTP_ERR_INVALID_ARG  # slack ring accepted
+    assert _windowed(_kv(capacity=24), ws_bytes=0) == W.WMTP_ERR_WORKSPACE
+
+
+def test_rollback_arguments_rejected_before_launch(lib):
+    L = W.lib()
+    assert L.wmtp_ring_rollback(None, FAKE, None) == W.WMTP_ERR_INVALID_ARG
+    assert L.wmtp_ring_rollback(ctypes.byref(_kv()), None, None) == W.WMTP_ERR_INVALID_ARG
+    assert L.wmtp_ring_rollback(ctypes.byref(_kv()), FAKE + 2, None) == W.WMTP_ERR_INVALID_ARG
+    assert L.wmtp_ring_rollback(ctypes.byref(_kv(head_dim=96)), FAKE, None) == W.WMTP_ERR_UNSUPPORTED
+
+
+def test_accept_arguments_rejected_before_launch(lib):
+    L = W.lib()
+    ws_need = L.wmtp_accept_workspace_bytes(2, 3, 1000)
+    assert ws_need > 0
+    assert L.wmtp_accept_workspace_bytes(0, 3, 1000) == 0
+    assert L.wmtp_accept_workspace_bytes(2, 64, 1000) == 0
+
+    def call(logits=FAKE, dtype=W.WMTP_BF16, batch=2, k=3, vocab=1000, draft=FAKE, out=FAKE,
+             ws=FAKE, ws_bytes=1 << 20):
+        return L.wmtp_greedy_accept(logits, dtype, batch, k, vocab, draft, out, out, out, out, ws,
+                                    ws_bytes, None)
+
+    assert call(dtype=7) == W.WMTP_ERR_UNSUPPORTED
+    assert call(logits=None) == W.WMTP_ERR_INVALID_ARG
+    assert call(logits=FAKE + 1) == W.WMTP_ERR_INVALID_ARG
+    assert call(dtype=W.WMTP_F32, logits=FAKE + 2) == W.WMTP_ERR_INVALID_ARG
+    assert call(draft=None) == W.WMTP_ERR_INVALID_ARG
+    assert call(k=-1) == W.WMTP_ERR_INVALID_ARG
+    assert call(k=64) == W.WMTP_ERR_INVALID_ARG
+    assert call(vocab=0) == W.WMTP_ERR_INVALID_ARG
+    assert call(out=None) == W.WMTP_ERR_INVALID_ARG
+    assert call(ws=None) == W.WMTP_ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == W.WMTP_ERR_WORKSPACE
+    assert call(ws_bytes=ws_need - 1) == W.WMTP_ERR_WORKSPACE

@@ -1,0 +1,198 @@
+"""GPU parity of the speculative-decoding steps around the draft attention: rings with slack
+slots, rollback of rejected draft tokens, windowed attention after rollbacks, and greedy
+acceptance from the target's logits. Ring tags, lengths and bytes must match the host model bit
+for bit; acceptance outputs are integers and must match the oracle exactly; attention matches the
+float64 oracle within the usual tolerances."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from draft_attention_amd import binding as W
+from draft_attention_amd import synth
+from gpu_common import DEV, TOL, compare, ocode, say, tdtype
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_ring(ring: W.KVCache, model: oracle.RingModel, seq_k, seq_v, what: str):
+    """Tags and lengths equal the model's; every occupied slot holds the bytes of the position
+    its tag names (seq_k/seq_v: host arrays [B][Hkv][positions][d] of the final content)."""
+    tags = ring.pos.cpu().numpy().astype(np.int64)
+    assert np.array_equal(tags, model.tags), f"{what}: position tags differ"
+    assert np.array_equal(ring.seq_len.cpu().numpy().astype(np.int64), model.n), f"{what}: seq_len"
+    hk, hv = synth.host_array(ring.k), synth.host_array(ring.v)
+    for b in range(ring.batch):
+        occ = model.occupied_slots(b)
+        pos = model.tags[b, occ]
+        assert np.array_equal(hk[b][:, occ], seq_k[b][:, pos]), f"{what}: K bytes of sequence {b}"
+        assert np.array_equal(hv[b][:, occ], seq_v[b][:, pos]), f"{what}: V bytes of sequence {b}"
+
+
+class _Spec:
+    """Device ring + host model + the final content of every position of every sequence. Draft
+    tokens of round r get their own seeded rows, so a position rewritten after a rollback holds
+    different bytes from the rejected token it replaces."""
+
+    def __init__(self, B, Hkv, d, S, Wn, slack, dt, seed):
+        self.B, self.Hkv, self.d, self.dt, self.seed = B, Hkv, d, dt, seed
+        self.ring = W.KVCache.ring(B, Hkv, d, S, Wn, tdtype(dt), slack=slack)
+        self.model = oracle.RingModel(B, S, Wn, slack)
+        self.seq_k = [np.zeros((Hkv, 0, d), dtype=self._np()) for _ in range(B)]
+        self.seq_v = [np.zeros((Hkv, 0, d), dtype=self._np()) for _ in range(B)]
+        self.round = 0
+
+    def _np(self):
+        return np.uint16 if self.dt == "bf16" else np.float32
+
+    def append(self, t: int):
+        """Append t tokens to every sequence in one call."""
+        self.round += 1
+        rows_k, rows_v = [], []
+        for b in range(self.B):
+            n = int(self.model.n[b])
+            sd = self.seed + 7919 * self.round
+            rows_k.append(synth.token_rows(sd, synth.KNEW_ID, b, n, n + t, self.Hkv, self.d,
+                                           tdtype(self.dt), DEV))
+            rows_v.append(synth.token_rows(sd, synth.VNEW_ID, b, n, n + t, self.Hkv, self.d,
+                                           tdtype(self.dt), DEV))
+        kn, vn = torch.stack(rows_k), torch.stack(rows_v)
+        W.wmtp_ring_append(self.ring, kn, vn, t)
+        hk, hv = synth.host_array(kn), synth.host_array(vn)  # [B][t][Hkv][d]
+        for b in range(self.B):
+            n = int(self.model.n[b])
+            keep = n  # positions >= n are replaced
+            self.seq_k[b] = np.concatenate([self.seq_k[b][:, :keep], hk[b].transpose(1, 0, 2)], 1)
+            self.seq_v[b] = np.concatenate([self.seq_v[b][:, :keep], hv[b].transpose(1, 0, 2)], 1)
+            self.model.append(b, t)
+
+    def rollback(self, drops):
+        W.wmtp_ring_rollback(self.ring, torch.tensor(drops, dtype=torch.int32, device=DEV))
+        for b, d in enumerate(drops):
+            expect = min(max(int(d), 0), self.model.max_rollback(b))
+            assert self.model.rollback(b, int(d)) == expect
+            n = int(self.model.n[b])
+            self.seq_k[b] = self.seq_k[b][:, :n]
+            self.seq_v[b] = self.seq_v[b][:, :n]
+
+    def logical_kv(self):
+        n_max = max(int(x) for x in self.model.n)
+        k = np.zeros((self.B, self.Hkv, n_max, self.d), dtype=self._np())
+        v = np.zeros_like(k)
+        for b in range(self.B):
+            k[b, :, :self.seq_k[b].shape[1]] = self.seq_k[b]
+            v[b, :, :self.seq_v[b].shape[1]] = self.seq_v[b]
+        return oracle.contiguous_kv(k, v, ocode(self.dt))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("S,Wn,slack", [(4, 16, 5), (0, 7, 3), (3, 1, 2), (4, 64, 6)])
+def test_append_and_rollback_bitexact(dt, S, Wn, slack):
+    B, Hkv, d = 3, 2, 128
+    say(f"ring slack append/rollback {dt} S={S} W={Wn} slack={slack}")
+    spec = _Spec(B, Hkv, d, S, Wn, slack, dt, seed=31)
+    rng = np.random.default_rng(S * 1000 + Wn * 10 + slack)
+    spec.append(S + Wn + slack + 9)  # prefill past one wrap
+    _check_ring(spec.ring, spec.model, spec.seq_k, spec.seq_v, "after prefill")
+    for step in range(12):
+        t = int(rng.integers(1, slack + 2))
+        spec.append(t)
+        drops = rng.integers(-1, slack + 3, size=B).tolist()  # includes clamped and negative
+        spec.rollback(drops)
+        _check_ring(spec.ring, spec.model, spec.seq_k, spec.seq_v, f"step {step}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("G,d", [(4, 64), (8, 128), (16, 256), (32, 128)])
+def test_windowed_attention_after_rollbacks(dt, G, d):
+    """A speculative loop: k drafts appended (each attended), some rejected and rolled back, a
+    correction appended. The windowed output at every draft step equals the oracle over the
+    logical sequence as it stands (sinks + last W positions), with slack slots skipped."""
+    B, Hkv, S, Wn, slack, k = 2, 2, 4, 48, 4, 4
+    Hq = G * Hkv
+    say(f"windowed after rollbacks {dt} G={G} d={d}")
+    spec = _Spec(B, Hkv, d, S, Wn, slack, dt, seed=77)
+    rng = np.random.default_rng(G * 100 + d)
+    scale = 1.0 / math.sqrt(d)
+    ws = W.workspace(B, Hq, Hkv, d, 1, spec.ring.capacity)
+    spec.append(150)
+    for it in range(6):
+        for i in range(k):
+            spec.append(1)
+            q = synth.queries(91, it * k + i, B, 1, Hq, d, tdtype(dt), DEV)
+            out = torch.full((B, 1, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+            lse = torch.full((B, 1, Hq), float("nan"), dtype=torch.float32, device=DEV)
+            W.wmtp_draft_attn_windowed(spec.ring, q, Hq, scale, out, lse, ws)
+            ro, rl = oracle.draft_windowed(synth.host_array(q), ocode(dt), spec.logical_kv(),
+                                           spec.model.n.tolist(), S, Wn, scale)
+            compare(out, lse, ro, rl, dt, f"iteration {it} draft {i}")
+        spec.rollback(rng.integers(0, k + 1, size=B).tolist())
+        spec.append(1)  # the target's correction / bonus token
+    _check_ring(spec.ring, spec.model, spec.seq_k, spec.seq_v, "end of loop")
+
+
+def _logits(B, k, V, dt, seed, ties=True):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((B, k + 1, V), generator=g, dtype=torch.float32)
+    if ties:  # copy each row's maximum to a second, later or earlier, index
+        for b in range(B):
+            for i in range(k + 1):
+                j = int(torch.argmax(x[b, i]))
+                x[b, i, (j + 1 + (b * 7 + i) % (V - 1)) % V] = x[b, i, j]
+    return x.to(torch.bfloat16 if dt == "bf16" else torch.float32)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,k,V", [(1, 5, 151936), (3, 4, 4096), (4, 1, 4097), (2, 0, 50),
+                                   (8, 7, 32000)])
+def test_greedy_accept_exact(dt, B, k, V):
+    say(f"greedy accept {dt} B={B} k={k} V={V}")
+    x = _logits(B, k, V, dt, seed=B * 100 + k * 10 + V % 97)
+    host = x.float().double().numpy()  # exact for bf16 and f32
+    choice_ref = np.argmax(host, axis=2)
+    rng = np.random.default_rng(V + k)
+    draft = np.empty((B, k), dtype=np.int64)
+    for b in range(B):  # accept a random prefix, then a mismatch (or all)
+        a = int(rng.integers(0, k + 1))
+        for i in range(k):
+            draft[b, i] = choice_ref[b, i] if i < a else (choice_ref[b, i] + 1) % V
+    ch_ref, acc_ref, nxt_ref, drop_ref = oracle.greedy_accept(host, draft)
+    xd = x.to(DEV)
+    dd = torch.tensor(draft, dtype=torch.int32, device=DEV)
+    choice = torch.full((B, k + 1), -7, dtype=torch.int32, device=DEV)
+    n_acc, nxt, drop = (torch.full((B,), -7, dtype=torch.int32, device=DEV) for _ in range(3))
+    ws = W.accept_workspace(B, k, V)
+    W.wmtp_greedy_accept(xd, k, dd, choice, n_acc, nxt, drop, ws)
+    assert np.array_equal(choice.cpu().numpy(), ch_ref)
+    assert np.array_equal(n_acc.cpu().numpy(), acc_ref)
+    assert np.array_equal(nxt.cpu().numpy(), nxt_ref)
+    assert np.array_equal(drop.cpu().numpy(), drop_ref)
+
+
+def test_accept_feeds_rollback_on_device():
+    """Verification outcome to ring state without the host: n_drop from wmtp_greedy_accept goes
+    straight into wmtp_ring_rollback on the same stream."""
+    B, Hkv, d, S, Wn, k, V = 4, 2, 128, 4, 32, 5, 1000
+    say("accept -> rollback chain")
+    spec = _Spec(B, Hkv, d, S, Wn, k, "bf16", seed=5)
+    spec.append(100)
+    spec.append(k)  # the k drafts
+    x = _logits(B, k, V, "bf16", seed=9, ties=False)
+    host = x.float().double().numpy()
+    choice_ref = np.argmax(host, axis=2)
+    draft = np.array([[choice_ref[b, i] if i < b else (choice_ref[b, i] + 3) % V for i in range(k)]
+                      for b in range(B)])
+    _, acc_ref, _, drop_ref = oracle.greedy_accept(host, draft)
+    assert acc_ref.tolist() == [0, 1, 2, 3]
+    choice = torch.empty((B, k + 1), dtype=torch.int32, device=DEV)
+    n_acc, nxt, drop = (torch.empty((B,), dtype=torch.int32, device=DEV) for _ in range(3))
+    W.wmtp_greedy_accept(x.to(DEV), k, torch.tensor(draft, dtype=torch.int32, device=DEV), choice,
+                         n_acc, nxt, drop, W.accept_workspace(B, k, V))
+    W.wmtp_ring_rollback(spec.ring, drop)
+    for b in range(B):
+        spec.model.rollback(b, int(drop_ref[b]))
+        n = int(spec.model.n[b])
+        spec.seq_k[b], spec.seq_v[b] = spec.seq_k[b][:, :n], spec.seq_v[b][:, :n]
+    _check_ring(spec.ring, spec.model, spec.seq_k, spec.seq_v, "after accept + rollback")

@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the context-length sweep of single calls")
+    ap.add_argument("--no-composite", action="store_true",
+                    help="skip the speculative decode-iteration composite")
     ap.add_argument("--graph", action="store_true",
                     help="replay each phase of the iteration as a captured HIP graph instead of "
                          "launching every call from Python")
@@ -128,7 +130,7 @@ def main():
 
     # ---------------- draft caches (million-token draft shapes)
     Hq, Hkv, d, S, Wn = D3.n_q_heads, D3.n_kv_heads, D3.head_dim, D3.sink, D3.window
-    cap = L + k * total_steps + 16
+    cap = L + k * total_steps + 16 + COMPOSITE_MARGIN
     log(f"setup: contiguous draft cache {Hkv}x{cap}x{d} bf16, ring {S}+{Wn}")
     full = W.KVCache.contiguous(1, Hkv, d, cap, dt, dev)
     fill_sequence(full.k[0], D3.seed, synth.K_ID, 0, 0, L, dt, dev)
@@ -153,7 +155,7 @@ def main():
 
     # ---------------- target cache (verify shapes)
     Hq4, Hkv4, d4 = V4.n_q_heads, V4.n_kv_heads, V4.head_dim
-    cap4 = L + m * total_steps + 16
+    cap4 = L + m * total_steps + 16 + COMPOSITE_MARGIN
     log(f"setup: target cache {Hkv4}x{cap4}x{d4} bf16")
     tgt = W.KVCache.contiguous(1, Hkv4, d4, cap4, dt, dev)
     fill_sequence(tgt.k[0], V4.seed, synth.K_ID, 0, 0, L, dt, dev)
@@ -258,6 +260,8 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             attn_only[name].append(e0.elapsed_time(e1))
+    comp = None if args.no_composite else composite(
+        W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log)
     read_ceiling = read_probe(W, probe_buf, probe_out, stream, ev)
     log(f"read probe: {read_ceiling:.1f} GB/s")
     sweep_res = None if args.no_sweep else sweep(
@@ -318,6 +322,7 @@ def main():
                       "attn_plus_append": round(mean_us["ver_step"], 2)},
         "dropped_kv_fraction": round(1.0 - win_slots / n_mid, 5),
         "read_probe_gbs": round(read_ceiling, 1),
+        "composite": comp,
         "sweep": sweep_res,
         "roofline": {
             "kernel": "full-context draft attention call (split-K attention + LSE merge, "
@@ -338,6 +343,119 @@ def main():
         result["cpu_baseline"] = cpu_baseline(full, tgt, ring, draft_q, ver_q, k, m, S, Wn,
                                               scale3, scale4, step_bytes, log)
     print(json.dumps(result), flush=True)
+
+
+COMPOSITE_VOCAB = 131072  # synthetic target vocabulary for the greedy acceptance step
+COMPOSITE_MARGIN = 512  # cache room for the tokens the composite keeps (a + 1 per iteration)
+
+
+def composite(W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log, iters: int = 8,
+              depths=(1, 2, 3, 4, 5)):
+    """One speculative decode iteration at L = 1M, attention side only, for draft depths k:
+    k draft steps (append + attend; windowed ring with k slack slots, or the contiguous cache),
+    the target's append + verification of the k+1 candidates, greedy acceptance on synthetic
+    logits, and the rollback of the rejected tokens in the draft cache and the target cache.
+    Also the no-speculation decode step (the target appends one token and attends everything).
+    Per-token cost for an acceptance of a drafts = iteration cost / (a + 1) tokens."""
+    import torch
+
+    dev = full.k.device
+    dt = full.k.dtype
+    Hq, Hkv, d, S, Wn = D3.n_q_heads, D3.n_kv_heads, D3.head_dim, D3.sink, D3.window
+    Hq4, Hkv4, d4 = V4.n_q_heads, V4.n_kv_heads, V4.head_dim
+    kmax = max(depths)
+    n0 = int(full.seq_len.item())
+    n4 = int(tgt.seq_len.item())
+    # a ring with kmax slack slots holding the same sequence as the contiguous draft cache
+    ring = W.KVCache.ring(1, Hkv, d, S, Wn, dt, dev, slack=kmax)
+    for p0, p1 in ((0, min(S, n0)), (max(S, n0 - Wn - kmax), n0)):
+        ring.seq_len.fill_(p0)
+        W.wmtp_ring_append(ring, full.k[0, :, p0:p1].permute(1, 0, 2).contiguous()[None],
+                           full.v[0, :, p0:p1].permute(1, 0, 2).contiguous()[None], p1 - p0)
+    scale3, scale4 = 1.0 / math.sqrt(d), 1.0 / math.sqrt(d4)
+    tok_k = synth.token_rows(D3.seed + 1, synth.KNEW_ID, 0, 0, kmax, Hkv, d, dt, dev)
+    tok_v = synth.token_rows(D3.seed + 1, synth.VNEW_ID, 0, 0, kmax, Hkv, d, dt, dev)
+    cand_k = synth.token_rows(V4.seed + 1, synth.KNEW_ID, 0, 0, kmax + 1, Hkv4, d4, dt, dev)
+    cand_v = synth.token_rows(V4.seed + 1, synth.VNEW_ID, 0, 0, kmax + 1, Hkv4, d4, dt, dev)
+    q3 = synth.queries(D3.seed + 1, 0, 1, 1, Hq, d, dt, dev)
+    q4 = synth.queries(V4.seed + 1, 0, 1, kmax + 1, Hq4, d4, dt, dev)
+    out3 = torch.empty((1, 1, Hq, d), dtype=torch.float32, device=dev)
+    lse3 = torch.empty((1, 1, Hq), dtype=torch.float32, device=dev)
+    out4 = torch.empty((1, kmax + 1, Hq4, d4), dtype=torch.float32, device=dev)
+    lse4 = torch.empty((1, kmax + 1, Hq4), dtype=torch.float32, device=dev)
+    ws_win = W.workspace(1, Hq, Hkv, d, 1, ring.capacity, dev)
+    ws_full = W.workspace(1, Hq, Hkv, d, 1, cap, dev)
+    V = COMPOSITE_VOCAB
+    g = torch.Generator(device="cpu").manual_seed(D3.seed)
+    logits = torch.randn((1, kmax + 1, V), generator=g).to(dt).to(dev)
+    drafts = torch.zeros((1, kmax), dtype=torch.int32, device=dev)
+    choice = torch.empty((1, kmax + 1), dtype=torch.int32, device=dev)
+    n_acc, nxt, n_drop = (torch.empty((1,), dtype=torch.int32, device=dev) for _ in range(3))
+    res = {"vocab": V, "depths": list(depths), "windowed_iter_us": [], "full_iter_us": [],
+           "reduction": [], "per_token_us": {}}
+
+    def iteration(form, k):
+        ws_acc = W.accept_workspace(1, k, V, dev)
+        ws_ver = W.workspace(1, Hq4, Hkv4, d4, k + 1, cap4, dev)
+        lg = logits[:, :k + 1].contiguous()
+        dr = drafts[:, :k].contiguous()
+        ch = choice[:, :k + 1].contiguous()
+
+        def run():
+            cache = ring if form == "windowed" else full
+            for i in range(k):
+                W.wmtp_ring_append(cache, tok_k[i:i + 1][None], tok_v[i:i + 1][None], 1)
+                if form == "windowed":
+                    W.wmtp_draft_attn_windowed(ring, q3, Hq, scale3, out3, lse3, ws_win)
+                else:
+                    W.wmtp_draft_attn_full(full, q3, Hq, scale3, cap, out3, lse3, ws_full)
+            W.wmtp_ring_append(tgt, cand_k[:k + 1][None], cand_v[:k + 1][None], k + 1)
+            W.wmtp_verify_attn(tgt, q4[:, :k + 1].contiguous(), k + 1, Hq4, scale4, cap4,
+                               out4[:, :k + 1], lse4[:, :k + 1], ws_ver)
+            W.wmtp_greedy_accept(lg, k, dr, ch, n_acc, nxt, n_drop, ws_acc)
+            W.wmtp_ring_rollback(cache, n_drop)
+            W.wmtp_ring_rollback(tgt, n_drop)
+        return run
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        marks = [ev() for _ in range(iters + 1)]
+        marks[0].record(stream)
+        for i in range(iters):
+            fn()
+            marks[i + 1].record(stream)
+        torch.cuda.synchronize()
+        us = sorted(1000.0 * marks[i].elapsed_time(marks[i + 1]) for i in range(iters))
+        return us[len(us) // 2]
+
+    for k in depths:
+        tw = timed(iteration("windowed", k))
+        tf = timed(iteration("full", k))
+        res["windowed_iter_us"].append(round(tw, 1))
+        res["full_iter_us"].append(round(tf, 1))
+        res["reduction"].append(round(1.0 - tw / tf, 4))
+        res["per_token_us"][str(k)] = {
+            "windowed": [round(tw / (a + 1), 1) for a in range(k + 1)],
+            "full": [round(tf / (a + 1), 1) for a in range(k + 1)]}
+        log(f"composite k={k}: windowed {tw:.1f} us, full {tf:.1f} us per iteration")
+    # caches are back where they started (every iteration rolls back what it did not keep)
+    assert int(full.seq_len.item()) >= n0 and int(tgt.seq_len.item()) >= n4
+    one_k = cand_k[:1][None]
+    one_v = cand_v[:1][None]
+    one = torch.ones((1,), dtype=torch.int32, device=dev)
+    ws1 = W.workspace(1, Hq4, Hkv4, d4, 1, cap4, dev)
+
+    def nospec():
+        W.wmtp_ring_append(tgt, one_k, one_v, 1)
+        W.wmtp_verify_attn(tgt, q4[:, :1].contiguous(), 1, Hq4, scale4, cap4, out4[:, :1],
+                           lse4[:, :1], ws1)
+        W.wmtp_ring_rollback(tgt, one)  # keep the cache length fixed across repetitions
+    res["no_speculation_step_us"] = round(timed(nospec), 1)
+    res["note"] = ("attention-side cost of one decode iteration (eager launches); tokens per "
+                   "iteration = accepted drafts a + 1; per_token_us[k][a] = iteration / (a+1); "
+                   "no_speculation_step_us includes a rollback of the token it appends")
+    return res
 
 
 def read_probe(W, buf, out, stream, ev, reps: int = 5) -> float:

@@ -541,7 +541,8 @@ struct Coop {
   static constexpr int kChunks = kRowBytes / 16;             // 16-byte chunks per key row
   static constexpr int kSwz = (kChunks < 16 ? kChunks : 16) - 1;
   static constexpr int kVSwz = (kChunks / 2 < 8 ? kChunks / 2 : 8) - 1;  // 32-byte segments of V
-  static constexpr int kSplitD = kWavesPerBlock / NB;         // wavefronts sharing a row block
+  static constexpr int kRbw = NB > kWavesPerBlock ? NB / kWavesPerBlock : 1;  // row blocks/wave
+  static constexpr int kSplitD = NB >= kWavesPerBlock ? 1 : kWavesPerBlock / NB;  // waves per block
   static constexpr int kDw = D / kSplitD;                     // output dims per wavefront
   static constexpr int kDpl = kDw / 16;                       // V dims per lane (= output blocks)
   static constexpr int kQRegs = BF16 ? D / 32 : D / 16;       // 16-byte Q/K pieces per lane
@@ -589,7 +590,8 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int rb = wave / C::kSplitD;  // row block of this wavefront
+  // row blocks of this wavefront: rb0 + 4*j, j < kRbw (NB = 8: blocks wave and wave + 4)
+  const int rb0 = wave / C::kSplitD;
   const int d0 = (wave % C::kSplitD) * C::kDw;
   const int split = blockIdx.x;
   const int bhc = blockIdx.y;
@@ -658,23 +660,26 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   // (otherwise the compiler drains every load there, once per round of kPrefetch tiles).
   // A padding row (past the last query row) loads the last real row instead of zeros: its
   // results are never written, and an unconditional load needs no wait before the prefetch.
-  const int row = chunk * chunk_rows + rb * 16 + r16;
-  const bool row_ok = row < row_end;
-  const int row_q = row_ok ? row : row_end - 1;
-  const int jq = row_q / G;
-  const int hq = h * G + row_q % G;
-  const int last_visible = (a.mode == kModeVerify) ? (n - a.m + jq) : (n - 1);
-  // the last key every row of the workgroup may attend (candidate 0 sees the fewest)
-  const int vis_all = min(last, (a.mode == kModeVerify) ? (n - a.m) : (n - 1));
-  QVec qf[C::kQRegs];
-  {
+  bool row_ok[C::kRbw];
+  int last_visible[C::kRbw];
+  QVec qf[C::kRbw][C::kQRegs];
+#pragma unroll
+  for (int j = 0; j < C::kRbw; ++j) {
+    const int row = chunk * chunk_rows + (rb0 + kWavesPerBlock * j) * 16 + r16;
+    row_ok[j] = row < row_end;
+    const int row_q = row_ok[j] ? row : row_end - 1;
+    const int jq = row_q / G;
+    const int hq = h * G + row_q % G;
+    last_visible[j] = (a.mode == kModeVerify) ? (n - a.m + jq) : (n - 1);
     const size_t qoff = ((size_t)(b * a.m + jq) * a.n_q_heads + hq) * D;
 #pragma unroll
     for (int ks = 0; ks < C::kQRegs; ++ks)
-      qf[ks] = __builtin_bit_cast(
+      qf[j][ks] = __builtin_bit_cast(
           QVec, *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + qoff * C::kEB +
                                                 (ks * 4 + grp) * 16));
   }
+  // the last key every row of the workgroup may attend (candidate 0 sees the fewest)
+  const int vis_all = min(last, (a.mode == kModeVerify) ? (n - a.m) : (n - 1));
 
   if (has_range) {
 #pragma unroll
@@ -682,11 +687,16 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   }
 
   const float scale_log2 = a.sm_scale * kLog2e;
-  float m_ref = -INFINITY;  // reference max (log2 units), shared by the row's four lanes
-  float l_lane = 0.f;       // this lane's share of the running sum
-  f32x4_t o[C::kDpl];
+  float m_ref[C::kRbw];   // reference max (log2 units), shared by the row's four lanes
+  float l_lane[C::kRbw];  // this lane's share of the running sum
+  f32x4_t o[C::kRbw][C::kDpl];
 #pragma unroll
-  for (int e = 0; e < C::kDpl; ++e) o[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < C::kRbw; ++j) {
+    m_ref[j] = -INFINITY;
+    l_lane[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < C::kDpl; ++e) o[j][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   // one 16-key tile: K at kt, V at kt + kTileBytes (swizzled LDS layout); i = the workgroup's
   // tile index (tiles past its share are computed fully masked)
@@ -694,68 +704,81 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
     const bool live = i < my_tiles;  // workgroup-uniform
     const int t0 = tile_start(i);
     const char* vt = kt + C::kTileBytes;
-    // ---- S^T (16 keys x 16 rows) for this row block
-    f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // ---- S^T (16 keys x 16 rows) for each of this wavefront's row blocks
+    f32x4_t sacc[C::kRbw];
+#pragma unroll
+    for (int j = 0; j < C::kRbw; ++j) sacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < C::kQRegs; ++ks) {
       const uint4 kv =
           *reinterpret_cast<const uint4*>(kt + coop_slot<D, NB, BF16>(r16, ks * 4 + grp, 0));
-      if constexpr (BF16) {
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qf[ks],
-                                                       sacc, 0, 0, 0);
-      } else {
-        const float4 kf = __builtin_bit_cast(float4, kv);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.x, qf[ks][0], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.y, qf[ks][1], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.z, qf[ks][2], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.w, qf[ks][3], sacc, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < C::kRbw; ++j) {
+        if constexpr (BF16) {
+          sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv),
+                                                            qf[j][ks], sacc[j], 0, 0, 0);
+        } else {
+          const float4 kf = __builtin_bit_cast(float4, kv);
+          sacc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.x, qf[j][ks][0], sacc[j], 0, 0, 0);
+          sacc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.y, qf[j][ks][1], sacc[j], 0, 0, 0);
+          sacc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.z, qf[j][ks][2], sacc[j], 0, 0, 0);
+          sacc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.w, qf[j][ks][3], sacc[j], 0, 0, 0);
+        }
       }
     }
 
     // ---- softmax with a lazily moved reference max (as in the split kernel)
-    const int vis = live ? min(last, last_visible) : -1;
-    float sc[4];
-    float mx = -INFINITY;
-    if (!RING && live && t0 + kTileKeys - 1 <= vis_all) {  // workgroup-uniform: none masked
+    float p[C::kRbw][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sc[j] = sacc[j] * scale_log2;
-        mx = fmaxf(mx, sc[j]);
+    for (int j = 0; j < C::kRbw; ++j) {
+      const int vis = live ? min(last, last_visible[j]) : -1;
+      float sc[4];
+      float mx = -INFINITY;
+      if (!RING && live && t0 + kTileKeys - 1 <= vis_all) {  // workgroup-uniform: none masked
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          sc[t] = sacc[j][t] * scale_log2;
+          mx = fmaxf(mx, sc[t]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int key = t0 + 4 * grp + t;
+          const bool ok = key <= vis && (!RING || rm.attended(key));
+          sc[t] = ok ? sacc[j][t] * scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sc[t]);
+        }
       }
-    } else {
+      if (__ballot(mx > m_ref[j] + kRescaleLog2)) {  // lane-local test first, as in the split kernel
+        mx = xgroup_max(mx);
+        const bool moved = mx > m_ref[j] + kRescaleLog2;
+        const float alpha = moved ? __builtin_amdgcn_exp2f(m_ref[j] - mx) : 1.f;
+        l_lane[j] *= alpha;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = t0 + 4 * grp + j;
-        const bool ok = key <= vis && (!RING || rm.attended(key));
-        sc[j] = ok ? sacc[j] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sc[j]);
+        for (int e = 0; e < C::kDpl; ++e) o[j][e] *= alpha;
+        m_ref[j] = moved ? mx : m_ref[j];
       }
-    }
-    if (__ballot(mx > m_ref + kRescaleLog2)) {  // lane-local test first, as in the split kernel
-      mx = xgroup_max(mx);
-      const bool moved = mx > m_ref + kRescaleLog2;
-      const float alpha = moved ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;
-      l_lane *= alpha;
+      const float m_use = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
 #pragma unroll
-      for (int e = 0; e < C::kDpl; ++e) o[e] *= alpha;
-      m_ref = moved ? mx : m_ref;
-    }
-    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-    float p[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = __builtin_amdgcn_exp2f(sc[j] - m_use);
-      l_lane += p[j];
+      for (int t = 0; t < 4; ++t) {
+        p[j][t] = __builtin_amdgcn_exp2f(sc[t] - m_use);
+        l_lane[j] += p[j][t];
+      }
     }
 
-    // ---- O^T (this wavefront's dims) += V^T . P^T
+    // ---- O^T (this wavefront's dims) += V^T . P^T, one V operand shared by the row blocks
     if constexpr (BF16) {
       // Block e covers dims d0 + 16e .. +15. The V^T operand (lane (r16, grp): keys 4*grp .. +3
       // of dim d0 + 16e + r16) comes from one transposing LDS read per block: within each 16-lane
       // group, lane 4j + q addresses the 8 bytes of key 4*grp + j at dims d0 + 16e + 4q .. +3,
       // and lane i receives element i % 4 of what lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4 address.
-      const bf16x4_t pb = __builtin_convertvector(f32x4_t{p[0], p[1], p[2], p[3]}, bf16x4_t);
-      const s16x4_t pop = __builtin_bit_cast(s16x4_t, pb);
+      s16x4_t pop[C::kRbw];
+#pragma unroll
+      for (int j = 0; j < C::kRbw; ++j) {
+        const bf16x4_t pb =
+            __builtin_convertvector(f32x4_t{p[j][0], p[j][1], p[j][2], p[j][3]}, bf16x4_t);
+        pop[j] = __builtin_bit_cast(s16x4_t, pb);
+      }
       const int vkey = 4 * grp + (r16 >> 2);
 #pragma unroll
       for (int e = 0; e < C::kDpl; ++e) {
@@ -764,7 +787,9 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
         typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
         const s16x4_t vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4_t*)(__attribute__((address_space(3))) const char*)src);
-        o[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, o[e], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < C::kRbw; ++j)
+          o[j][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop[j], o[j][e], 0, 0, 0);
       }
     } else {
       // lane r16 owns dims d0 + kDpl*r16 + e: one key row's kDpl consecutive dims per lane
@@ -786,11 +811,13 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int j = 0; j < C::kRbw; ++j)
 #pragma unroll
-        for (int e = 0; e < C::kDpl; ++e)
-          o[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, vw[u][e]), p[u],
-                                                      o[e], 0, 0, 0);
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < C::kDpl; ++e)
+            o[j][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, vw[u][e]),
+                                                           p[j][u], o[j][e], 0, 0, 0);
     }
   };
 
@@ -812,34 +839,39 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   }
 
   // ---- this wavefront's part of the workgroup's partial
-  const float l_row = xgroup_sum(l_lane);
-  if (!row_ok) return;
   const size_t part = (size_t)bhc * n_splits + split;
   constexpr int kRows = 16 * NB;
-  const int rloc = rb * 16 + r16;
-  float* dst = a.ws_o + (part * kRows + rloc) * D + d0;
-  if constexpr (BF16) {
-    // lane (r16, grp) holds O^T rows 4*grp + j of block e: dims d0 + 16e + 4*grp + j
 #pragma unroll
-    for (int e = 0; e < C::kDpl; ++e)
-      *reinterpret_cast<float4*>(dst + 16 * e + 4 * grp) = make_float4(o[e][0], o[e][1], o[e][2], o[e][3]);
-  } else {
-    // lane (r16, grp) holds O^T rows 4*grp + j of block e: dim d0 + kDpl*(4*grp + j) + e
+  for (int j = 0; j < C::kRbw; ++j) {
+    const float l_row = xgroup_sum(l_lane[j]);
+    if (!row_ok[j]) continue;
+    const int rloc = (rb0 + kWavesPerBlock * j) * 16 + r16;
+    float* dst = a.ws_o + (part * kRows + rloc) * D + d0;
+    if constexpr (BF16) {
+      // lane (r16, grp) holds O^T rows 4*grp + t of block e: dims d0 + 16e + 4*grp + t
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float* d = dst + C::kDpl * (4 * grp + j);
-      if constexpr (C::kDpl >= 4) {
+      for (int e = 0; e < C::kDpl; ++e)
+        *reinterpret_cast<float4*>(dst + 16 * e + 4 * grp) =
+            make_float4(o[j][e][0], o[j][e][1], o[j][e][2], o[j][e][3]);
+    } else {
+      // lane (r16, grp) holds O^T rows 4*grp + t of block e: dim d0 + kDpl*(4*grp + t) + e
 #pragma unroll
-        for (int e = 0; e < C::kDpl; e += 4)
-          *reinterpret_cast<float4*>(d + e) = make_float4(o[e][j], o[e + 1][j], o[e + 2][j], o[e + 3][j]);
-      } else {
+      for (int t = 0; t < 4; ++t) {
+        float* d = dst + C::kDpl * (4 * grp + t);
+        if constexpr (C::kDpl >= 4) {
 #pragma unroll
-        for (int e = 0; e < C::kDpl; ++e) d[e] = o[e][j];
+          for (int e = 0; e < C::kDpl; e += 4)
+            *reinterpret_cast<float4*>(d + e) =
+                make_float4(o[j][e][t], o[j][e + 1][t], o[j][e + 2][t], o[j][e + 3][t]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < C::kDpl; ++e) d[e] = o[j][e][t];
+        }
       }
     }
+    if (d0 == 0 && grp == 0)
+      *reinterpret_cast<float2*>(a.ws_ml + (part * kRows + rloc) * 2) = make_float2(m_ref[j], l_row);
   }
-  if (d0 == 0 && grp == 0)
-    *reinterpret_cast<float2*>(a.ws_ml + (part * kRows + rloc) * 2) = make_float2(m_ref, l_row);
 }
 
 // One workgroup per (output row, 64 dims). 16 threads cover the 64 dims as float4 columns; 16
@@ -991,6 +1023,14 @@ hipError_t launch_coop(const AttnArgs& a, const SplitPlan& p, hipStream_t stream
         else attn_coop_kernel<D, 4, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
       }
       break;
+    case 8:
+      if constexpr (BF16 && D <= 128) {
+        if (ring) attn_coop_kernel<D, 8, BF16, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
+        else attn_coop_kernel<D, 8, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
+      } else {
+        return hipErrorInvalidValue;
+      }
+      break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -1019,16 +1059,19 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
   // each with the workgroup count measured best for it on MI355X
   p->coop = kAllowCoop && p->rows > 16;
   const int target_blocks = p->coop ? kTargetBlocksCoop : kTargetBlocksSplit;
-  // fp32 with head_dim 256 keeps at most two row blocks per workgroup (register budget)
-  const int coop_cap = (dtype == WMTP_F32 && head_dim == 256) ? 32 : kWavesPerBlock * 16;
+  // row blocks per cooperative workgroup within the register budget: eight (two per wavefront)
+  // for bf16 up to head_dim 128, two for fp32 at head_dim 256, four otherwise
+  const int coop_cap = (dtype == WMTP_BF16 && head_dim <= 128) ? 2 * kWavesPerBlock * 16
+                       : (dtype == WMTP_F32 && head_dim == 256) ? 32 : kWavesPerBlock * 16;
   const int cap = p->coop ? coop_cap : rows_cap(dtype, head_dim);
   p->chunk_rows = p->rows < cap ? p->rows : cap;
   p->n_chunks = (p->rows + p->chunk_rows - 1) / p->chunk_rows;
   p->nr = (p->chunk_rows + 15) / 16;
   if (p->coop) {
-    // row blocks per workgroup: 1, 2 or 4 (the wavefronts split the rest by dims); a bf16 lane
-    // needs at least two dims, so head_dim 64 keeps two row blocks
+    // row blocks per workgroup: 1, 2, 4 (the wavefronts split the rest by dims) or 8 (two per
+    // wavefront); a bf16 lane needs at least two dims, so head_dim 64 keeps two row blocks
     if (p->nr == 3) p->nr = 4;
+    if (p->nr > 4) p->nr = 8;
     if (dtype == WMTP_BF16 && head_dim == 64 && p->nr < 2) p->nr = 2;
   }
   const long long bhc = (long long)batch * n_kv_heads * p->n_chunks;

@@ -178,6 +178,9 @@ VERIFY_CASES = [
     ("f32", 64, 8, 2, 4, [4097, 2]),
     ("f32", 128, 8, 1, 3, [999]),
     ("bf16", 128, 8, 4, 16, [2000]),
+    ("bf16", 128, 32, 2, 6, [3000, 77]),  # 96 rows: one chunk, two row blocks per wavefront
+    ("bf16", 128, 16, 1, 8, [2500]),      # 128 rows
+    ("bf16", 64, 32, 2, 5, [1234]),       # 80 rows at head_dim 64
 ]
 
 

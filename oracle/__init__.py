@@ -33,6 +33,8 @@ here (listed with reasons in the design notes of the repository):
   "restore exactly the state before the rejected tokens were appended";
 * greedy acceptance: draft token i is kept while it equals the target's argmax at row i (lowest
   index on ties); the target's argmax at the first rejected row is the next token;
+* MASW working memory (MASW page, section 4.1): sinks, the exact local window and every memory
+  slot materialised so far; slot rows are given (the adaptor that makes them is out of scope);
 * verification query j of m (the candidates sit at positions n-m .. n-1) attends positions
   0 .. n-m+j, its own included;
 * outputs and lse are float64 here; lse uses the natural log; an empty set gives o = 0 and
@@ -74,9 +76,12 @@ def build(verbose: bool = False) -> str:
     return _LIB_PATH
 
 
+_RUNS = 4  # position runs per problem (ORACLE_RUNS in wmtp_oracle.c)
+
+
 class _Problem(ctypes.Structure):
-    _fields_ = [("q_off", ctypes.c_int64), ("kv_off", ctypes.c_int64 * 2),
-                ("count", ctypes.c_int64 * 2), ("row_stride", ctypes.c_int64),
+    _fields_ = [("q_off", ctypes.c_int64), ("kv_off", ctypes.c_int64 * _RUNS),
+                ("count", ctypes.c_int64 * _RUNS), ("row_stride", ctypes.c_int64),
                 ("out_off", ctypes.c_int64)]
 
 
@@ -320,15 +325,15 @@ def attention(q: np.ndarray, q_dtype: int, kv: LogicalKV, sets, scale: float,
     for b in range(B):
         for j in range(m):
             ranges = [r for r in sets[b][j] if r[1] > r[0]]
-            if len(ranges) > 2:
-                raise ValueError("at most two position ranges per problem")
+            if len(ranges) > _RUNS:
+                raise ValueError(f"at most {_RUNS} position ranges per problem")
             for hq in range(Hq):
                 h = hq // G
                 pr = probs[i]
                 pr.q_off = ((b * m + j) * Hq + hq) * d
                 pr.row_stride = d
                 pr.out_off = ((b * m + j) * Hq + hq) * d
-                for run in range(2):
+                for run in range(_RUNS):
                     if run < len(ranges):
                         r0, cnt = kv.row_run(b, ranges[run][0], ranges[run][1])
                         pr.kv_off[run] = ((b * Hkv + h) * R + r0) * d
@@ -359,6 +364,36 @@ def draft_windowed(q, q_dtype, kv: LogicalKV, n: Sequence[int], S: int, W: int, 
     """Windowed-MTP draft step over the logical sequence: sinks plus the last W positions."""
     sets = [[windowed_positions(int(n[b]), S, W)] for b in range(q.shape[0])]
     return attention(q, q_dtype, kv, sets, scale, nthreads)
+
+
+SLOT_BASE = 1 << 40  # label of memory slot j in a MASW working set: SLOT_BASE + j
+
+
+def masw_kv(kv: LogicalKV, slots_k: np.ndarray, slots_v: np.ndarray) -> LogicalKV:
+    """The raw rows of ``kv`` followed by memory-slot rows ``[B][Hkv][M][d]`` (same dtype), slot j
+    labelled with position SLOT_BASE + j."""
+    B, Hkv, R, d = kv.k.shape
+    M = slots_k.shape[2]
+    k = np.concatenate([kv.k, slots_k.astype(kv.k.dtype)], axis=2)
+    v = np.concatenate([kv.v, slots_v.astype(kv.v.dtype)], axis=2)
+    segments = [list(kv.segments[b]) + [(SLOT_BASE, R, M)] for b in range(B)]
+    return LogicalKV(k, v, kv.dtype, segments)
+
+
+def masw_positions(n: int, S: int, W: int, n_slots: int) -> List[Range]:
+    """MASW working memory (MASW page, section 4.1): the sink tokens, the exact local window and
+    the memory slots materialised so far, each once."""
+    return windowed_positions(n, S, W) + [(SLOT_BASE, SLOT_BASE + max(0, n_slots))]
+
+
+def draft_masw(q, q_dtype, kv: LogicalKV, n: Sequence[int], S: int, W: int, slots_k, slots_v,
+               n_slots: Sequence[int], scale: float, nthreads: int = 0):
+    """MASW-style draft step: one query token per sequence attends the sinks and the last W of
+    its n_b raw positions plus its first n_slots[b] memory slots (the slot rows are inputs; how
+    a slot is materialised from history is the adaptor's business and not computed here)."""
+    both = masw_kv(kv, slots_k, slots_v)
+    sets = [[masw_positions(int(n[b]), S, W, int(n_slots[b]))] for b in range(q.shape[0])]
+    return attention(q, q_dtype, both, sets, scale, nthreads)
 
 
 def verify(q, q_dtype, kv: LogicalKV, n: Sequence[int], scale: float, nthreads: int = 0):

@@ -20,7 +20,8 @@
  * This is the plain definition written out: two passes over A, float64 throughout, no online
  * rescaling, no splitting of A, no blocking. bf16 inputs are widened exactly (a bf16 value is the
  * top 16 bits of a float32). Which rows form A (sinks, window, causal verify prefix) is decided by
- * the Python side of the oracle, which passes each problem's rows as up to two contiguous runs.
+ * the Python side of the oracle, which passes each problem's rows as up to ORACLE_RUNS contiguous
+ * runs (sinks, the recent window and, for the MASW layout, the memory slots).
  *
  * Degenerate case (a reading; the pages are silent): an empty set gives o = 0 and lse = -inf.
  *
@@ -35,13 +36,14 @@
 #endif
 
 enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
+#define ORACLE_RUNS 4
 
 /* One attention problem: a query vector and the rows it attends. Row r of run s starts at element
  * kv_off[s] + r * row_stride of the K and V arrays. All offsets are in elements. */
 typedef struct {
   int64_t q_off;       /* element offset of the query vector in q */
-  int64_t kv_off[2];   /* element offset of the first row of each run */
-  int64_t count[2];    /* rows in each run (0 for an unused run) */
+  int64_t kv_off[ORACLE_RUNS]; /* element offset of the first row of each run */
+  int64_t count[ORACLE_RUNS];  /* rows in each run (0 for an unused run) */
   int64_t row_stride;  /* elements between consecutive rows of a run */
   int64_t out_off;     /* element offset of the output vector in out; lse index is out_off / d */
 } wmtp_oracle_problem;
@@ -59,7 +61,8 @@ static double load_elem(const void* base, int32_t dtype, int64_t i) {
 static void solve_one(const wmtp_oracle_problem* pr, int32_t d, int32_t dtype_q, int32_t dtype_kv,
                       const void* q, const void* k, const void* v, double scale, double* out,
                       double* lse) {
-  int64_t n = pr->count[0] + pr->count[1];
+  int64_t n = 0;
+  for (int run = 0; run < ORACLE_RUNS; ++run) n += pr->count[run];
   double* o = out + pr->out_off;
   for (int32_t i = 0; i < d; ++i) o[i] = 0.0;
   if (n <= 0) {
@@ -73,7 +76,7 @@ static void solve_one(const wmtp_oracle_problem* pr, int32_t d, int32_t dtype_q,
   /* pass 1: scores and their maximum */
   int64_t j = 0;
   double M = -INFINITY;
-  for (int run = 0; run < 2; ++run) {
+  for (int run = 0; run < ORACLE_RUNS; ++run) {
     for (int64_t r = 0; r < pr->count[run]; ++r, ++j) {
       int64_t base = pr->kv_off[run] + r * pr->row_stride;
       double dot = 0.0;
@@ -85,7 +88,7 @@ static void solve_one(const wmtp_oracle_problem* pr, int32_t d, int32_t dtype_q,
   /* pass 2: normaliser and weighted sum of values */
   double Z = 0.0;
   j = 0;
-  for (int run = 0; run < 2; ++run) {
+  for (int run = 0; run < ORACLE_RUNS; ++run) {
     for (int64_t r = 0; r < pr->count[run]; ++r, ++j) {
       int64_t base = pr->kv_off[run] + r * pr->row_stride;
       double w = exp(s[j] - M);
@@ -108,8 +111,12 @@ int wmtp_oracle_attention(int64_t nprob, const wmtp_oracle_problem* probs, int32
                           int32_t nthreads) {
   if (nprob < 0 || d <= 0 || (nprob > 0 && (!probs || !q || !out || !lse))) return 1;
   for (int64_t p = 0; p < nprob; ++p) {
-    if (probs[p].count[0] < 0 || probs[p].count[1] < 0) return 1;
-    if ((probs[p].count[0] + probs[p].count[1]) > 0 && (!k || !v)) return 1;
+    int64_t total = 0;
+    for (int run = 0; run < ORACLE_RUNS; ++run) {
+      if (probs[p].count[run] < 0) return 1;
+      total += probs[p].count[run];
+    }
+    if (total > 0 && (!k || !v)) return 1;
     if (probs[p].out_off % d != 0) return 1;
   }
 #ifdef _OPENMP

@@ -585,3 +585,62 @@ def test_greedy_accept_matches_plain_loops():
                 a += 1
             assert ch[b].tolist() == picks
             assert n_acc[b] == a and nxt[b] == picks[a] and drop[b] == k - a
+
+
+# ------------------------------------------------------------------------------------------
+# MASW working memory: sinks + memory slots + local window (MASW page, section 4.1)
+# ------------------------------------------------------------------------------------------
+def _masw_case(seed, n, M, d=8, Hq=4, Hkv=2):
+    q = _rand((1, 1, Hq, d), seed)
+    k = _rand((1, Hkv, n, d), seed + 1)
+    v = _rand((1, Hkv, n, d), seed + 2)
+    sk = _rand((1, Hkv, M, d), seed + 3)
+    sv = _rand((1, Hkv, M, d), seed + 4)
+    return q, k, v, sk, sv
+
+
+def test_masw_without_slots_is_the_windowed_draft(oracle_lib):
+    q, k, v, sk, sv = _masw_case(90, 50, 6)
+    kv = oracle.contiguous_kv(k, v, F64)
+    o1, l1 = oracle.draft_masw(q, F64, kv, [50], 4, 8, sk, sv, [0], 0.3)
+    o2, l2 = oracle.draft_windowed(q, F64, kv, [50], 4, 8, 0.3)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("n,S,W,m", [(50, 4, 8, 6), (9, 4, 8, 3), (40, 0, 5, 1), (3, 4, 8, 5)])
+def test_masw_matches_torch_sdpa_over_the_union(oracle_lib, n, S, W, m):
+    """P4-style pin: torch SDPA (float64) over the explicitly concatenated working set."""
+    q, k, v, sk, sv = _masw_case(100 + n, n, 6)
+    kv = oracle.contiguous_kv(k, v, F64)
+    o, l = oracle.draft_masw(q, F64, kv, [n], S, W, sk, sv, [m], 0.35)
+    keep = [p for p in range(n) if p < S or p >= n - W]
+    kk = np.concatenate([k[:, :, keep], sk[:, :, :m]], axis=2)
+    vv = np.concatenate([v[:, :, keep], sv[:, :, :m]], axis=2)
+    masks = np.ones((1, 1, kk.shape[2]), dtype=bool)
+    ro, rl = _sdpa(q, kk, vv, masks, 0.35)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, rl, rtol=0, atol=1e-12)
+
+
+def test_masw_is_the_lse_merge_of_window_and_slots(oracle_lib):
+    """Partition identity: the union's result is the log-sum-exp merge of the windowed part and
+    the slots-only part."""
+    q, k, v, sk, sv = _masw_case(130, 60, 7)
+    kv = oracle.contiguous_kv(k, v, F64)
+    o, l = oracle.draft_masw(q, F64, kv, [60], 4, 8, sk, sv, [7], 0.3)
+    ow, lw = oracle.draft_windowed(q, F64, kv, [60], 4, 8, 0.3)
+    slots_only = oracle.contiguous_kv(sk, sv, F64)
+    os_, ls = oracle.draft_full(q, F64, slots_only, [7], 0.3)
+    L = np.logaddexp(lw, ls)
+    merged = ow * np.exp(lw - L)[..., None] + os_ * np.exp(ls - L)[..., None]
+    np.testing.assert_allclose(o, merged, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l, L, rtol=0, atol=1e-13)
+
+
+def test_masw_spike_in_a_slot_returns_that_slot(oracle_lib):
+    q, k, v, sk, sv = _masw_case(140, 30, 5, d=4, Hq=2, Hkv=1)
+    q[:] = 1.0
+    sk[0, 0, 3] = 60.0  # one slot key scores 240 x scale above the rest
+    kv = oracle.contiguous_kv(k, v, F64)
+    o, _ = oracle.draft_masw(q, F64, kv, [30], 2, 6, sk, sv, [5], 1.0)
+    np.testing.assert_allclose(o[0, 0, 0], sv[0, 0, 3], rtol=0, atol=1e-12)

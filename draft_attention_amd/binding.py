@@ -64,6 +64,9 @@ def lib():
         L.wmtp_status_string.argtypes = [ctypes.c_int]
         L.wmtp_status_string.restype = ctypes.c_char_p
         L.wmtp_ring_rollback.argtypes = [kvp, vp, vp]
+        L.wmtp_draft_attn_masw.argtypes = [kvp, kvp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
+        L.wmtp_masw_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.wmtp_masw_workspace_bytes.restype = sz
         L.wmtp_greedy_accept.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.wmtp_accept_workspace_bytes.argtypes = [i32, i32, i32]
         L.wmtp_accept_workspace_bytes.restype = sz
@@ -71,6 +74,7 @@ def lib():
         L.wmtp_llc_flush.argtypes = [vp, sz, ctypes.c_uint8, vp]
         for name in ("wmtp_ring_append", "wmtp_draft_attn_windowed", "wmtp_draft_attn_full",
                      "wmtp_verify_attn", "wmtp_ring_rollback", "wmtp_greedy_accept",
+                     "wmtp_draft_attn_masw",
                      "wmtp_probe_read", "wmtp_llc_flush"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -276,6 +280,36 @@ def wmtp_llc_flush(buf, value: int = 0, stream=None, check=True) -> int:
     n = buf.numel() * buf.element_size()
     st = lib().wmtp_llc_flush(_ptr(buf), int(n), int(value) & 0xFF, _stream(stream))
     return _done(st, "wmtp_llc_flush", check)
+
+
+def wmtp_draft_attn_masw(ring, slots, q, n_q_heads: int, sm_scale: float, max_slots: int, out,
+                         lse, ws, ws_bytes: Optional[int] = None, stream=None, check=True) -> int:
+    """MASW draft step: ring sinks + last W positions, plus memory slots 0..slots.seq_len[b]-1."""
+    _check_attn(ring, q, 1, n_q_heads, out, lse)
+    r, sl = _desc(ring), _desc(slots)
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    st = lib().wmtp_draft_attn_masw(ctypes.byref(r), ctypes.byref(sl), _ptr(q), int(n_q_heads),
+                                    float(sm_scale), int(max_slots), _ptr(out), _ptr(lse),
+                                    _ptr(ws), int(nbytes), _stream(stream))
+    return _done(st, "wmtp_draft_attn_masw", check)
+
+
+def wmtp_masw_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, ring_capacity,
+                              max_slots) -> int:
+    return int(lib().wmtp_masw_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
+                                               ring_capacity, max_slots))
+
+
+def masw_workspace(batch, n_q_heads, n_kv_heads, head_dim, ring_capacity, max_slots,
+                   device="cuda"):
+    import torch
+
+    n = wmtp_masw_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, ring_capacity, max_slots)
+    if n == 0:
+        raise ValueError("wmtp_draft_attn_masw does not accept these sizes")
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]
 
 
 def wmtp_ring_rollback(cache, n_drop, stream=None, check=True) -> int:

@@ -79,8 +79,28 @@ int attention_call(const wmtp_kv* c, const void* q, int m, int n_q_heads, float 
   a.sink = c->sink;
   a.window = c->window;
   a.wphys = c->window >= 1 ? c->capacity - c->sink : 0;
+  a.part_stride = plan.n_splits;
+  a.part_offset = 0;
   hipError_t e = wmtp::launch_attention(a, plan, c->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WMTP_OK : WMTP_ERR_HIP;
+}
+
+// Plans of the two reads of a MASW draft step (the ring's sinks + window, the memory slots). Both
+// have the same row chunking (one query token, same heads and dtype); their partials share one
+// merge. Returns false when no call accepts the sizes.
+bool masw_plans(const wmtp_kv* ring, int n_q_heads, int max_slots, SplitPlan* pr, SplitPlan* ps) {
+  return wmtp::make_plan_for(ring->batch, n_q_heads, ring->n_kv_heads, ring->head_dim, 1,
+                             ring->capacity, ring->dtype, pr) &&
+         wmtp::make_plan_for(ring->batch, n_q_heads, ring->n_kv_heads, ring->head_dim, 1,
+                             max_slots, ring->dtype, ps);
+}
+
+size_t masw_bytes(const SplitPlan& pr, const SplitPlan& ps) {
+  SplitPlan both = pr;
+  both.n_splits = pr.n_splits + ps.n_splits;
+  both.ws_o_floats = pr.ws_o_floats + ps.ws_o_floats;
+  both.ws_ml_floats = pr.ws_ml_floats + ps.ws_ml_floats;
+  return plan_bytes(both);
 }
 
 }  // namespace
@@ -144,6 +164,92 @@ int wmtp_verify_attn(const wmtp_kv* cache, const void* q, int32_t m, int32_t n_q
   if (max_seq_len < 1 || max_seq_len > cache->capacity) return WMTP_ERR_INVALID_ARG;
   return attention_call(cache, q, m, n_q_heads, sm_scale, max_seq_len, wmtp::kModeVerify, out, lse,
                         ws, ws_bytes, stream);
+}
+
+int wmtp_draft_attn_masw(const wmtp_kv* ring, const wmtp_kv* slots, const void* q,
+                         int32_t n_q_heads, float sm_scale, int32_t max_slots, float* out,
+                         float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_kv(ring);
+  if (st != WMTP_OK) return st;
+  st = check_kv(slots);
+  if (st != WMTP_OK) return st;
+  if (ring->window < 1 || slots->window != 0) return WMTP_ERR_INVALID_ARG;
+  if (slots->batch != ring->batch || slots->n_kv_heads != ring->n_kv_heads ||
+      slots->head_dim != ring->head_dim || slots->dtype != ring->dtype)
+    return WMTP_ERR_INVALID_ARG;
+  if (max_slots < 1 || max_slots > slots->capacity) return WMTP_ERR_INVALID_ARG;
+  if (!q || !out) return WMTP_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4))) return WMTP_ERR_INVALID_ARG;
+  if (n_q_heads < ring->n_kv_heads || n_q_heads % ring->n_kv_heads) return WMTP_ERR_INVALID_ARG;
+  if (!isfinite(sm_scale)) return WMTP_ERR_INVALID_ARG;
+  SplitPlan pr, ps;
+  if (!masw_plans(ring, n_q_heads, max_slots, &pr, &ps)) return WMTP_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < masw_bytes(pr, ps)) return WMTP_ERR_WORKSPACE;
+
+  const int total = pr.n_splits + ps.n_splits;
+  const size_t o_floats = pr.ws_o_floats + ps.ws_o_floats;
+  wmtp::AttnArgs a;
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.ws_o = static_cast<float*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(o_floats * sizeof(float), kAlign));
+  a.batch = ring->batch;
+  a.n_kv_heads = ring->n_kv_heads;
+  a.n_q_heads = n_q_heads;
+  a.head_dim = ring->head_dim;
+  a.m = 1;
+  a.sm_scale = sm_scale;
+  a.part_stride = total;
+  // read 1: the ring's sinks and last `window` positions (partials 0 .. pr.n_splits-1)
+  a.k = ring->k;
+  a.v = ring->v;
+  a.seq_len = ring->seq_len;
+  a.capacity = ring->capacity;
+  a.limit = ring->capacity;
+  a.mode = wmtp::kModeWindowed;
+  a.sink = ring->sink;
+  a.window = ring->window;
+  a.wphys = ring->capacity - ring->sink;
+  a.part_offset = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = wmtp::launch_partials(a, pr, ring->dtype, s);
+  if (e != hipSuccess) return WMTP_ERR_HIP;
+  // read 2: memory slots 0 .. slots->seq_len[b]-1 (partials pr.n_splits .. total-1)
+  wmtp::AttnArgs b = a;
+  b.k = slots->k;
+  b.v = slots->v;
+  b.seq_len = slots->seq_len;
+  b.capacity = slots->capacity;
+  b.limit = max_slots;
+  b.mode = wmtp::kModeFull;
+  b.sink = slots->sink;
+  b.window = 0;
+  b.wphys = 0;
+  b.part_offset = pr.n_splits;
+  e = wmtp::launch_partials(b, ps, ring->dtype, s);
+  if (e != hipSuccess) return WMTP_ERR_HIP;
+  e = wmtp::launch_merge(a, pr, total, s);
+  return e == hipSuccess ? WMTP_OK : WMTP_ERR_HIP;
+}
+
+size_t wmtp_masw_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, int32_t ring_capacity, int32_t max_slots) {
+  size_t best = 0;
+  const int dtypes[2] = {WMTP_F32, WMTP_BF16};
+  for (int dt : dtypes) {
+    wmtp_kv r = {};
+    r.batch = batch;
+    r.n_kv_heads = n_kv_heads;
+    r.head_dim = head_dim;
+    r.capacity = ring_capacity;
+    r.dtype = dt;
+    SplitPlan pr, ps;
+    if (!masw_plans(&r, n_q_heads, max_slots, &pr, &ps)) return 0;
+    const size_t bytes = masw_bytes(pr, ps);
+    if (bytes > best) best = bytes;
+  }
+  return best;
 }
 
 int wmtp_ring_rollback(const wmtp_kv* cache, const int32_t* n_drop, void* stream) {

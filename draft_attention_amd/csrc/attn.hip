@@ -475,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   __syncthreads();
   if (wave != 0) return;
 
-  const size_t part = (size_t)bhc * n_splits + split;
+  const size_t part = (size_t)bhc * a.part_stride + a.part_offset + split;
 #pragma unroll
   for (int rb = 0; rb < NR; ++rb) {
     const int rloc = rb * 16 + r16;
@@ -839,7 +839,7 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   }
 
   // ---- this wavefront's part of the workgroup's partial
-  const size_t part = (size_t)bhc * n_splits + split;
+  const size_t part = (size_t)bhc * a.part_stride + a.part_offset + split;
   constexpr int kRows = 16 * NB;
 #pragma unroll
   for (int j = 0; j < C::kRbw; ++j) {
@@ -994,10 +994,6 @@ hipError_t launch_split(const AttnArgs& a, const SplitPlan& p, hipStream_t strea
       default: if constexpr (kMaxNr >= 4) attn_split_kernel<D, 4, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
     }
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  merge_kernel<D><<<dim3(a.batch * a.m * a.n_q_heads, D / 64), dim3(256), 0, stream>>>(
-      a, p.n_splits, p.n_chunks, p.chunk_rows, p.nr);
   return hipGetLastError();
 }
 
@@ -1033,10 +1029,6 @@ hipError_t launch_coop(const AttnArgs& a, const SplitPlan& p, hipStream_t stream
       break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  merge_kernel<D><<<dim3(a.batch * a.m * a.n_q_heads, D / 64), dim3(256), 0, stream>>>(
-      a, p.n_splits, p.n_chunks, p.chunk_rows, p.nr);
   return hipGetLastError();
 }
 
@@ -1089,7 +1081,29 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
   return true;
 }
 
+template <int D>
+hipError_t launch_merge(const AttnArgs& a, const SplitPlan& p, int total_splits, hipStream_t stream) {
+  merge_kernel<D><<<dim3(a.batch * a.m * a.n_q_heads, D / 64), dim3(256), 0, stream>>>(
+      a, total_splits, p.n_chunks, p.chunk_rows, p.nr);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const AttnArgs& a, const SplitPlan& p, int total_splits, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 64: return launch_merge<64>(a, p, total_splits, stream);
+    case 128: return launch_merge<128>(a, p, total_splits, stream);
+    case 256: return launch_merge<256>(a, p, total_splits, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_attention(const AttnArgs& a, const SplitPlan& p, int dtype, hipStream_t stream) {
+  hipError_t e = launch_partials(a, p, dtype, stream);
+  if (e != hipSuccess) return e;
+  return launch_merge(a, p, a.part_stride, stream);
+}
+
+hipError_t launch_partials(const AttnArgs& a, const SplitPlan& p, int dtype, hipStream_t stream) {
   const bool bf16 = dtype == WMTP_BF16;
   if (p.coop) {
     switch (a.head_dim) {

@@ -66,9 +66,16 @@ struct AttnArgs {
   // i for the min(S, n) sinks, else in slot S + (w0 - S + i - sinks) mod wphys with
   // w0 = max(sinks, n - window). With wphys == window the attended keys are slots 0..limit-1.
   int sink, window, wphys;
+  // partial results of split s of (sequence, KV head, chunk) bhc go to index
+  // bhc * part_stride + part_offset + s (two launches can fill one merge: MASW working memory)
+  int part_stride, part_offset;
 };
 
+// split kernel (or cooperative kernel) writing partials, then the log-sum-exp merge over
+// part_stride partials per (sequence, KV head, chunk)
 hipError_t launch_attention(const AttnArgs& a, const SplitPlan& p, int dtype, hipStream_t stream);
+hipError_t launch_partials(const AttnArgs& a, const SplitPlan& p, int dtype, hipStream_t stream);
+hipError_t launch_merge(const AttnArgs& a, const SplitPlan& p, int total_splits, hipStream_t stream);
 
 struct AppendArgs {
   void* k;

@@ -138,6 +138,26 @@ int wmtp_verify_attn(const wmtp_kv* cache, const void* q, int32_t m, int32_t n_q
                      float sm_scale, int32_t max_seq_len, float* out, float* lse, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* MASW-style draft step (MASW page, section 4.1: the working memory is the sink tokens, an exact
+ * local window and compressed memory slots): one query token per sequence attends its ring's sinks
+ * and last `window` positions (exactly as wmtp_draft_attn_windowed) together with memory slots
+ * 0 .. slots->seq_len[b]-1 of `slots`, a contiguous cache (window = 0) holding one K/V row per
+ * materialised slot, appended by the caller (wmtp_ring_append) as slots are made; how a slot is
+ * made from history is not this library's business. Both caches must share batch, n_kv_heads,
+ * head_dim and dtype. max_slots is a host bound on every slots->seq_len[b]
+ * (1 <= max_slots <= slots->capacity), used only to size the launch. The two reads write one set
+ * of split partials and one log-sum-exp merge combines them, so the result is softmax attention
+ * over the union. out/lse as for the windowed call.
+ * ws: at least wmtp_masw_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, ring->capacity,
+ * max_slots) bytes. Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+int wmtp_draft_attn_masw(const wmtp_kv* ring, const wmtp_kv* slots, const void* q,
+                         int32_t n_q_heads, float sm_scale, int32_t max_slots, float* out,
+                         float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of wmtp_draft_attn_masw; 0 for sizes it rejects. */
+size_t wmtp_masw_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, int32_t ring_capacity, int32_t max_slots);
+
 /* Discard the newest n_drop[b] tokens of every sequence b after a rejected speculation (the MASW
  * page, section 4.3: rejected speculative local KV is discarded). n_drop is device memory [batch],
  * typically written by wmtp_greedy_accept on the same stream. The count is clamped on the device

@@ -32,7 +32,8 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"wmtp_ring_append", "wmtp_draft_attn_windowed", "wmtp_draft_attn_full",
                           "wmtp_verify_attn", "wmtp_attn_workspace_bytes", "wmtp_status_string",
                           "wmtp_probe_read", "wmtp_llc_flush", "wmtp_ring_rollback",
-                          "wmtp_greedy_accept", "wmtp_accept_workspace_bytes"}
+                          "wmtp_greedy_accept", "wmtp_accept_workspace_bytes",
+                          "wmtp_draft_attn_masw", "wmtp_masw_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -187,3 +188,27 @@ def test_accept_arguments_rejected_before_launch(lib):
     assert call(ws=None) == W.WMTP_ERR_WORKSPACE
     assert call(ws=FAKE + 16) == W.WMTP_ERR_WORKSPACE
     assert call(ws_bytes=ws_need - 1) == W.WMTP_ERR_WORKSPACE
+
+
+def test_masw_arguments_rejected_before_launch(lib):
+    L = W.lib()
+    ring = _kv()
+    slots = _kv(**CONTIG)
+    need = L.wmtp_masw_workspace_bytes(2, 8, 2, 128, 20, 64)
+    assert need > 0
+
+    def call(r=ring, sl=slots, q=FAKE, hq=8, max_slots=64, ws=FAKE, ws_bytes=1 << 30):
+        return L.wmtp_draft_attn_masw(ctypes.byref(r), ctypes.byref(sl), q, hq, 0.1, max_slots,
+                                      FAKE, None, ws, ws_bytes, None)
+
+    assert call(r=_kv(**CONTIG)) == W.WMTP_ERR_INVALID_ARG       # first cache must be a ring
+    assert call(sl=_kv()) == W.WMTP_ERR_INVALID_ARG               # slots must be contiguous
+    assert call(sl=_kv(**CONTIG, head_dim=64)) == W.WMTP_ERR_INVALID_ARG
+    assert call(sl=_kv(**CONTIG, dtype=W.WMTP_F32)) == W.WMTP_ERR_INVALID_ARG
+    assert call(sl=_kv(**CONTIG, batch=3)) == W.WMTP_ERR_INVALID_ARG
+    assert call(max_slots=0) == W.WMTP_ERR_INVALID_ARG
+    assert call(max_slots=65) == W.WMTP_ERR_INVALID_ARG
+    assert call(q=None) == W.WMTP_ERR_INVALID_ARG
+    assert call(hq=7) == W.WMTP_ERR_INVALID_ARG
+    assert call(ws=None) == W.WMTP_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == W.WMTP_ERR_WORKSPACE

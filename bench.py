@@ -260,6 +260,8 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             attn_only[name].append(e0.elapsed_time(e1))
+    masw_res = None if args.no_composite else masw_step(
+        W, synth, D3, full, ring, Hq, scale3, stream, ev, log)
     comp = None if args.no_composite else composite(
         W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log)
     read_ceiling = read_probe(W, probe_buf, probe_out, stream, ev)
@@ -323,6 +325,7 @@ def main():
         "dropped_kv_fraction": round(1.0 - win_slots / n_mid, 5),
         "read_probe_gbs": round(read_ceiling, 1),
         "composite": comp,
+        "masw": masw_res,
         "sweep": sweep_res,
         "roofline": {
             "kernel": "full-context draft attention call (split-K attention + LSE merge, "
@@ -455,6 +458,52 @@ def composite(W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log, iters: in
     res["note"] = ("attention-side cost of one decode iteration (eager launches); tokens per "
                    "iteration = accepted drafts a + 1; per_token_us[k][a] = iteration / (a+1); "
                    "no_speculation_step_us includes a rollback of the token it appends")
+    return res
+
+
+MASW_INTERVALS = (64, 8)  # raw tokens per memory slot
+
+
+def masw_step(W, synth, D3, full, ring, Hq, scale, stream, ev, log, calls: int = 30):
+    """MASW-style draft step at the million-token draft shapes: the ring's sinks + window plus
+    one memory slot per r raw tokens (synthetic slot rows), for each r in MASW_INTERVALS.
+    Median of back-to-back calls; algorithmic bytes = attended K/V rows + q + out."""
+    import torch
+
+    dev = full.k.device
+    dt = full.k.dtype
+    Hkv, d, S, Wn = D3.n_kv_heads, D3.head_dim, D3.sink, D3.window
+    n = int(ring.seq_len.item())
+    q = synth.queries(D3.seed + 2, 0, 1, 1, Hq, d, dt, dev)
+    out = torch.empty((1, 1, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((1, 1, Hq), dtype=torch.float32, device=dev)
+    res = {"context": n, "interval": [], "slots": [], "attn_us": [], "hbm_gbs": []}
+    for r in MASW_INTERVALS:
+        m = n // r
+        slots = W.KVCache.contiguous(1, Hkv, d, m, dt, dev)
+        for c0 in range(0, m, 1 << 16):  # synthetic slot rows, appended in pieces
+            c1 = min(m, c0 + (1 << 16))
+            W.wmtp_ring_append(slots, synth.token_rows(D3.seed + 3, 11, 0, c0, c1, Hkv, d, dt, dev)[None],
+                               synth.token_rows(D3.seed + 3, 12, 0, c0, c1, Hkv, d, dt, dev)[None],
+                               c1 - c0)
+        ws = W.masw_workspace(1, Hq, Hkv, d, ring.capacity, m, dev)
+        call = lambda: W.wmtp_draft_attn_masw(ring, slots, q, Hq, scale, m, out, lse, ws)
+        call()
+        marks = [ev() for _ in range(calls + 1)]
+        torch.cuda.synchronize()
+        marks[0].record(stream)
+        for i in range(calls):
+            call()
+            marks[i + 1].record(stream)
+        torch.cuda.synchronize()
+        us = sorted(1000.0 * marks[i].elapsed_time(marks[i + 1]) for i in range(calls))[calls // 2]
+        nbytes = 2 * (min(n, S + Wn) + m) * Hkv * d * 2 + Hq * d * 2 + Hq * (d + 1) * 4
+        res["interval"].append(r)
+        res["slots"].append(m)
+        res["attn_us"].append(round(us, 2))
+        res["hbm_gbs"].append(round(nbytes / (us * 1e-6) / 1e9, 1))
+        log(f"masw r={r}: {m} slots, {us:.2f} us")
+        del slots, ws
     return res
 
 

@@ -22,7 +22,7 @@
 // (o unnormalised, running max in log2 units, running sum) per query row.
 //
 // Kernel 2 (merge_kernel): log-sum-exp merge of the partials of every output row, one workgroup per
-// (row, 64 dims):
+// (row, 32 or 64 dims):
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  o = sum_s o_s 2^(m_s - M) / L,  lse = (M + log2 L) ln 2.
 
 #include <type_traits>
@@ -874,22 +874,23 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   }
 }
 
-// One workgroup per (output row, 64 dims). 16 threads cover the 64 dims as float4 columns; 16
-// lanes of splits stride over the partials in one online pass (each lane keeps its own running max
-// and rescales), with all loads of an unrolled batch independent; the lanes then combine through
-// LDS with the same rescaling rule.
-template <int D>
+// One workgroup per (output row, 4*COLS dims). COLS threads cover the dims as float4 columns;
+// 256/COLS lanes of splits stride over the partials in one online pass (each lane keeps its own
+// running max and rescales), a batch of COLS independent loads per lane covering 256 splits; the
+// lanes then combine through LDS with the same rescaling rule. Measured on MI355X: 8 columns are
+// faster for the draft steps' 65-128 splits per row, 16 for verification's 256.
+template <int D, int COLS>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, int n_chunks,
                                                     int chunk_rows, int nr) {
-  constexpr int kCols = 16;
+  constexpr int kCols = COLS;
   constexpr int kSplitLanes = 256 / kCols;
-  constexpr int kBatch = 16;
+  constexpr int kBatch = COLS;
   __shared__ float red_m[256];
   __shared__ float4 red_o[256];
   __shared__ float red_l[256];
 
   const int row_id = blockIdx.x;  // ((b * m + j) * Hq + hq)
-  const int dim0 = blockIdx.y * 64;
+  const int dim0 = blockIdx.y * (4 * kCols);
   const int hq = row_id % a.n_q_heads;
   const int bj = row_id / a.n_q_heads;
   const int j = bj % a.m;
@@ -1034,6 +1035,11 @@ hipError_t launch_coop(const AttnArgs& a, const SplitPlan& p, hipStream_t stream
 
 }  // namespace
 
+#ifndef WMTP_MIN_TILES_PER_WAVE
+#define WMTP_MIN_TILES_PER_WAVE 1
+#endif
+constexpr long long kMinTilesPerWave = WMTP_MIN_TILES_PER_WAVE;
+
 // Largest row chunk whose Q operand and O accumulators fit the register file beside the K/V tiles.
 static int rows_cap(int dtype, int head_dim) {
   if (dtype == WMTP_BF16) return head_dim == 256 ? 32 : 64;
@@ -1068,11 +1074,13 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
   }
   const long long bhc = (long long)batch * n_kv_heads * p->n_chunks;
   const long long tiles_per_seq = ((long long)max_seq_len + kTileKeys - 1) / kTileKeys;
-  // about target_blocks workgroups in all, but at least one tile per wavefront
-  long long blocks = (bhc * tiles_per_seq + kWavesPerBlock - 1) / kWavesPerBlock;
+  // about target_blocks workgroups in all, but at least kMinTilesPerWave tiles per wavefront
+  long long blocks = (bhc * tiles_per_seq + kWavesPerBlock * kMinTilesPerWave - 1) /
+                     (kWavesPerBlock * kMinTilesPerWave);
   if (blocks > target_blocks) blocks = target_blocks;
   long long per = (blocks + bhc - 1) / bhc;
-  const long long cap_per = (tiles_per_seq + kWavesPerBlock - 1) / kWavesPerBlock;
+  const long long cap_per =
+      (tiles_per_seq + kWavesPerBlock * kMinTilesPerWave - 1) / (kWavesPerBlock * kMinTilesPerWave);
   if (per > cap_per) per = cap_per;
   if (per < 1) per = 1;
   p->n_splits = (int)per;
@@ -1083,8 +1091,13 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
 
 template <int D>
 hipError_t launch_merge(const AttnArgs& a, const SplitPlan& p, int total_splits, hipStream_t stream) {
-  merge_kernel<D><<<dim3(a.batch * a.m * a.n_q_heads, D / 64), dim3(256), 0, stream>>>(
-      a, total_splits, p.n_chunks, p.chunk_rows, p.nr);
+  const unsigned rows = a.batch * a.m * a.n_q_heads;
+  if (total_splits > 128)
+    merge_kernel<D, 16><<<dim3(rows, D / 64), dim3(256), 0, stream>>>(a, total_splits, p.n_chunks,
+                                                                     p.chunk_rows, p.nr);
+  else
+    merge_kernel<D, 8><<<dim3(rows, D / 32), dim3(256), 0, stream>>>(a, total_splits, p.n_chunks,
+                                                                    p.chunk_rows, p.nr);
   return hipGetLastError();
 }
 

@@ -174,19 +174,24 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     # the three phases of a decode iteration, and their attention-only parts
+    # a draft step appends its token and attends: one fused call (wmtp_draft_step_*)
     def win_phase(s: int, append: bool = True):
         for i in range(k):
             t = s * k + i
             if append:
-                W.wmtp_ring_append(ring, draft_k[t:t + 1][None], draft_v[t:t + 1][None], 1)
-            W.wmtp_draft_attn_windowed(ring, draft_q[t], Hq, scale3, out3, lse3, ws_win)
+                W.wmtp_draft_step_windowed(ring, draft_k[t:t + 1][None], draft_v[t:t + 1][None],
+                                           draft_q[t], Hq, scale3, out3, lse3, ws_win)
+            else:
+                W.wmtp_draft_attn_windowed(ring, draft_q[t], Hq, scale3, out3, lse3, ws_win)
 
     def full_phase(s: int, append: bool = True):
         for i in range(k):
             t = s * k + i
             if append:
-                W.wmtp_ring_append(full, draft_k[t:t + 1][None], draft_v[t:t + 1][None], 1)
-            W.wmtp_draft_attn_full(full, draft_q[t], Hq, scale3, cap, out3, lse3, ws_full)
+                W.wmtp_draft_step_full(full, draft_k[t:t + 1][None], draft_v[t:t + 1][None],
+                                       draft_q[t], Hq, scale3, cap, out3, lse3, ws_full)
+            else:
+                W.wmtp_draft_attn_full(full, draft_q[t], Hq, scale3, cap, out3, lse3, ws_full)
 
     def ver_phase(s: int, append: bool = True):
         if append:
@@ -407,11 +412,12 @@ def composite(W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log, iters: in
         def run():
             cache = ring if form == "windowed" else full
             for i in range(k):
-                W.wmtp_ring_append(cache, tok_k[i:i + 1][None], tok_v[i:i + 1][None], 1)
                 if form == "windowed":
-                    W.wmtp_draft_attn_windowed(ring, q3, Hq, scale3, out3, lse3, ws_win)
+                    W.wmtp_draft_step_windowed(ring, tok_k[i:i + 1][None], tok_v[i:i + 1][None],
+                                               q3, Hq, scale3, out3, lse3, ws_win)
                 else:
-                    W.wmtp_draft_attn_full(full, q3, Hq, scale3, cap, out3, lse3, ws_full)
+                    W.wmtp_draft_step_full(full, tok_k[i:i + 1][None], tok_v[i:i + 1][None], q3,
+                                           Hq, scale3, cap, out3, lse3, ws_full)
             W.wmtp_ring_append(tgt, cand_k[:k + 1][None], cand_v[:k + 1][None], k + 1)
             W.wmtp_verify_attn(tgt, q4[:, :k + 1].contiguous(), k + 1, Hq4, scale4, cap4,
                                out4[:, :k + 1], lse4[:, :k + 1], ws_ver)

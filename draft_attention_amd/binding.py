@@ -64,6 +64,8 @@ def lib():
         L.wmtp_status_string.argtypes = [ctypes.c_int]
         L.wmtp_status_string.restype = ctypes.c_char_p
         L.wmtp_ring_rollback.argtypes = [kvp, vp, vp]
+        L.wmtp_draft_step_windowed.argtypes = [kvp, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+        L.wmtp_draft_step_full.argtypes = [kvp, vp, vp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
         L.wmtp_draft_attn_masw.argtypes = [kvp, kvp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
         L.wmtp_masw_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
         L.wmtp_masw_workspace_bytes.restype = sz
@@ -74,7 +76,7 @@ def lib():
         L.wmtp_llc_flush.argtypes = [vp, sz, ctypes.c_uint8, vp]
         for name in ("wmtp_ring_append", "wmtp_draft_attn_windowed", "wmtp_draft_attn_full",
                      "wmtp_verify_attn", "wmtp_ring_rollback", "wmtp_greedy_accept",
-                     "wmtp_draft_attn_masw",
+                     "wmtp_draft_attn_masw", "wmtp_draft_step_windowed", "wmtp_draft_step_full",
                      "wmtp_probe_read", "wmtp_llc_flush"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -280,6 +282,33 @@ def wmtp_llc_flush(buf, value: int = 0, stream=None, check=True) -> int:
     n = buf.numel() * buf.element_size()
     st = lib().wmtp_llc_flush(_ptr(buf), int(n), int(value) & 0xFF, _stream(stream))
     return _done(st, "wmtp_llc_flush", check)
+
+
+def wmtp_draft_step_windowed(ring, k_new, v_new, q, n_q_heads: int, sm_scale: float, out, lse, ws,
+                             ws_bytes: Optional[int] = None, stream=None, check=True) -> int:
+    """Append one token per sequence, then the windowed draft attention (one call)."""
+    _check_append(ring, k_new, v_new, 1)
+    _check_attn(ring, q, 1, n_q_heads, out, lse)
+    d = _desc(ring)
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    st = lib().wmtp_draft_step_windowed(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                        int(n_q_heads), float(sm_scale), _ptr(out), _ptr(lse),
+                                        _ptr(ws), int(nbytes), _stream(stream))
+    return _done(st, "wmtp_draft_step_windowed", check)
+
+
+def wmtp_draft_step_full(cache, k_new, v_new, q, n_q_heads: int, sm_scale: float,
+                         max_seq_len: int, out, lse, ws, ws_bytes: Optional[int] = None,
+                         stream=None, check=True) -> int:
+    """Append one token per sequence, then the full-context draft attention (one call)."""
+    _check_append(cache, k_new, v_new, 1)
+    _check_attn(cache, q, 1, n_q_heads, out, lse)
+    d = _desc(cache)
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    st = lib().wmtp_draft_step_full(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                    int(n_q_heads), float(sm_scale), int(max_seq_len), _ptr(out),
+                                    _ptr(lse), _ptr(ws), int(nbytes), _stream(stream))
+    return _done(st, "wmtp_draft_step_full", check)
 
 
 def wmtp_draft_attn_masw(ring, slots, q, n_q_heads: int, sm_scale: float, max_slots: int, out,

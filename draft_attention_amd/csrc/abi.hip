@@ -44,10 +44,41 @@ int check_kv(const wmtp_kv* c) {
   return WMTP_OK;
 }
 
+int append_call(const wmtp_kv* cache, const void* k_new, const void* v_new, int32_t n_new,
+                void* stream) {
+  int st = check_kv(cache);
+  if (st != WMTP_OK) return st;
+  if (n_new < 0) return WMTP_ERR_INVALID_ARG;
+  if (n_new == 0) return WMTP_OK;
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return WMTP_ERR_INVALID_ARG;
+  if (cache->window == 0 && n_new > cache->capacity) return WMTP_ERR_CAPACITY;
+  wmtp::AppendArgs a;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.pos = cache->pos;
+  a.seq_len = cache->seq_len;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.batch = cache->batch;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.capacity = cache->capacity;
+  a.sink = cache->sink;
+  a.window = cache->window == 0 ? 0 : cache->capacity - cache->sink;  // physical window
+  a.n_new = n_new;
+  a.elem_bytes = elem_bytes(cache->dtype);
+  hipError_t e = wmtp::launch_append(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WMTP_OK : WMTP_ERR_HIP;
+}
+
+
+// new_k/new_v (nullable): a fused draft step appends one token per sequence first. The split
+// kernel does both in one launch; a cooperative-kernel shape appends with the append kernel first.
 int attention_call(const wmtp_kv* c, const void* q, int m, int n_q_heads, float sm_scale,
                    int limit, int mode, float* out, float* lse, void* ws, size_t ws_bytes,
-                   void* stream) {
+                   void* stream, const void* new_k = nullptr, const void* new_v = nullptr) {
   if (!q || !out) return WMTP_ERR_INVALID_ARG;
+  if (new_k && (!new_v || !aligned(new_k, 16) || !aligned(new_v, 16))) return WMTP_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4))) return WMTP_ERR_INVALID_ARG;
   if (n_q_heads < c->n_kv_heads || n_q_heads % c->n_kv_heads) return WMTP_ERR_INVALID_ARG;
   if (!isfinite(sm_scale)) return WMTP_ERR_INVALID_ARG;
@@ -57,7 +88,7 @@ int attention_call(const wmtp_kv* c, const void* q, int m, int n_q_heads, float 
     return WMTP_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, kAlign) || ws_bytes < plan_bytes(plan)) return WMTP_ERR_WORKSPACE;
 
-  wmtp::AttnArgs a;
+  wmtp::AttnArgs a{};  // every field zero (no fused append, no partial offset) unless set
   a.q = q;
   a.k = c->k;
   a.v = c->v;
@@ -81,6 +112,16 @@ int attention_call(const wmtp_kv* c, const void* q, int m, int n_q_heads, float 
   a.wphys = c->window >= 1 ? c->capacity - c->sink : 0;
   a.part_stride = plan.n_splits;
   a.part_offset = 0;
+  if (new_k) {
+    if (plan.coop) {
+      const int st = append_call(c, new_k, new_v, 1, stream);
+      if (st != WMTP_OK) return st;
+    } else {
+      a.new_k = new_k;
+      a.new_v = new_v;
+      a.pos = c->pos;
+    }
+  }
   hipError_t e = wmtp::launch_attention(a, plan, c->dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WMTP_OK : WMTP_ERR_HIP;
 }
@@ -109,30 +150,30 @@ extern "C" {
 
 int wmtp_ring_append(const wmtp_kv* cache, const void* k_new, const void* v_new, int32_t n_new,
                      void* stream) {
+  return append_call(cache, k_new, v_new, n_new, stream);
+}
+
+int wmtp_draft_step_windowed(const wmtp_kv* ring, const void* k_new, const void* v_new,
+                             const void* q, int32_t n_q_heads, float sm_scale, float* out,
+                             float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_kv(ring);
+  if (st != WMTP_OK) return st;
+  if (ring->window < 1 || !k_new || !v_new) return WMTP_ERR_INVALID_ARG;
+  return attention_call(ring, q, 1, n_q_heads, sm_scale, ring->capacity, wmtp::kModeWindowed, out,
+                        lse, ws, ws_bytes, stream, k_new, v_new);
+}
+
+int wmtp_draft_step_full(const wmtp_kv* cache, const void* k_new, const void* v_new, const void* q,
+                         int32_t n_q_heads, float sm_scale, int32_t max_seq_len, float* out,
+                         float* lse, void* ws, size_t ws_bytes, void* stream) {
   int st = check_kv(cache);
   if (st != WMTP_OK) return st;
-  if (n_new < 0) return WMTP_ERR_INVALID_ARG;
-  if (n_new == 0) return WMTP_OK;
-  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return WMTP_ERR_INVALID_ARG;
-  if (cache->window == 0 && n_new > cache->capacity) return WMTP_ERR_CAPACITY;
-  wmtp::AppendArgs a;
-  a.k = cache->k;
-  a.v = cache->v;
-  a.pos = cache->pos;
-  a.seq_len = cache->seq_len;
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.batch = cache->batch;
-  a.n_kv_heads = cache->n_kv_heads;
-  a.head_dim = cache->head_dim;
-  a.capacity = cache->capacity;
-  a.sink = cache->sink;
-  a.window = cache->window == 0 ? 0 : cache->capacity - cache->sink;  // physical window
-  a.n_new = n_new;
-  a.elem_bytes = elem_bytes(cache->dtype);
-  hipError_t e = wmtp::launch_append(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? WMTP_OK : WMTP_ERR_HIP;
+  if (cache->window != 0 || !k_new || !v_new) return WMTP_ERR_INVALID_ARG;
+  if (max_seq_len < 1 || max_seq_len > cache->capacity) return WMTP_ERR_INVALID_ARG;
+  return attention_call(cache, q, 1, n_q_heads, sm_scale, max_seq_len, wmtp::kModeFull, out, lse,
+                        ws, ws_bytes, stream, k_new, v_new);
 }
+
 
 int wmtp_draft_attn_windowed(const wmtp_kv* ring, const void* q, int32_t n_q_heads, float sm_scale,
                              float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
@@ -188,7 +229,7 @@ int wmtp_draft_attn_masw(const wmtp_kv* ring, const wmtp_kv* slots, const void* 
 
   const int total = pr.n_splits + ps.n_splits;
   const size_t o_floats = pr.ws_o_floats + ps.ws_o_floats;
-  wmtp::AttnArgs a;
+  wmtp::AttnArgs a{};  // every field zero (no fused append, no partial offset) unless set
   a.q = q;
   a.out = out;
   a.lse = lse;

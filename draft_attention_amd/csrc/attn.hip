@@ -91,18 +91,23 @@ struct Tile {
 };
 
 // Keys t0..t0+15 (indices past `last` read row `last`; their scores are masked).
+// The slot `fresh` (-1: none) is read from the rows knew/vnew instead of the cache: the token a
+// fused draft step appends, whose slot is written in the same launch.
 template <int D, bool BF16>
 __device__ __forceinline__ void load_tile(const char* kbase, const char* vbase, int t0, int last,
-                                          int r16, int grp, Tile<D, BF16>& T) {
+                                          int r16, int grp, Tile<D, BF16>& T, int fresh = -1,
+                                          const char* knew = nullptr, const char* vnew = nullptr) {
   using F = Frag<D, BF16>;
   const int key = min(t0 + r16, last);
-  const uint4* kp = reinterpret_cast<const uint4*>(kbase + (size_t)key * D * F::kEB);
+  const char* krow = key == fresh ? knew : kbase + (size_t)key * D * F::kEB;
+  const uint4* kp = reinterpret_cast<const uint4*>(krow);
 #pragma unroll
   for (int ks = 0; ks < F::kQRegs; ++ks) T.k[ks] = stream_load16(kp + ks * 4 + grp);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int kv = min(t0 + 4 * grp + t, last);
-    const char* vp = vbase + ((size_t)kv * D + r16 * F::kDpl) * F::kEB;
+    const char* vrow = kv == fresh ? vnew : vbase + (size_t)kv * D * F::kEB;
+    const char* vp = vrow + (size_t)r16 * F::kDpl * F::kEB;
 #pragma unroll
     for (int st = 0; st < F::kSets; ++st) {
       if constexpr (F::kVWords == 4) {
@@ -338,7 +343,7 @@ constexpr bool pipelined() {
   return q + o + 2 * tile <= 224 && o <= 96;
 }
 
-template <int D, int NR, bool BF16, bool RING>
+template <int D, int NR, bool BF16, bool RING, bool FUSED>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_splits,
                                                               int n_chunks, int chunk_rows) {
   using F = Frag<D, BF16>;
@@ -362,15 +367,41 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
 
   int n = a.seq_len[b];
   n = max(n, 0);
+  const size_t head_off = (size_t)(b * a.n_kv_heads + h) * (size_t)a.capacity * D * F::kEB;
+  const char* kbase = static_cast<const char*>(a.k) + head_off;
+  const char* vbase = static_cast<const char*>(a.v) + head_off;
+  // fused draft step: the token at position n (its slot `fresh`) joins the attended set
+  int fresh = -1;
+  const char* knew = nullptr;
+  const char* vnew = nullptr;
+  if constexpr (FUSED) {
+    const int64_t p = n;
+    const int64_t slot = a.wphys == 0 ? p : (p < a.sink ? p : a.sink + (p - a.sink) % a.wphys);
+    const size_t new_off = (size_t)(b * a.n_kv_heads + h) * D * F::kEB;
+    knew = static_cast<const char*>(a.new_k) + new_off;
+    vnew = static_cast<const char*>(a.new_v) + new_off;
+    if (slot < a.capacity) {
+      fresh = (int)slot;
+      if (split == 0 && chunk == 0) {  // one workgroup per KV head stores the token
+        constexpr int kPieces = D * F::kEB / 16;
+        const int i = threadIdx.x;
+        if (i < kPieces)
+          reinterpret_cast<uint4*>(const_cast<char*>(kbase) + (size_t)slot * D * F::kEB)[i] =
+              reinterpret_cast<const uint4*>(knew)[i];
+        else if (i < 2 * kPieces)
+          reinterpret_cast<uint4*>(const_cast<char*>(vbase) + (size_t)slot * D * F::kEB)[i - kPieces] =
+              reinterpret_cast<const uint4*>(vnew)[i - kPieces];
+        if (h == 0 && i == 0 && a.pos) a.pos[(size_t)b * a.capacity + slot] = (int32_t)p;
+      }
+    }
+    n = n < 0x7fffffff ? n + 1 : n;
+  }
   const RingMask rm = ring_mask(a, n);
   n = min(n, a.limit);
   const int last = n - 1;
 
   const int r16 = lane & 15;
   const int grp = lane >> 4;
-  const size_t head_off = (size_t)(b * a.n_kv_heads + h) * (size_t)a.capacity * D * F::kEB;
-  const char* kbase = static_cast<const char*>(a.k) + head_off;
-  const char* vbase = static_cast<const char*>(a.v) + head_off;
 
   // Tiles are dealt grid-stride: wavefront (split, wave) takes tiles (split*4 + wave) + k*(4*
   // n_splits), so all workgroups sweep the cache together (the access pattern HBM streams best);
@@ -385,7 +416,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   // The first tile is requested against the host-side bound (a.limit >= 1, so row limit-1 is
   // always a valid address) without waiting for seq_len: the loads overlap the seq_len read, and
   // seq_len only masks. Later tiles clamp to the last real key.
-  if (t < a.limit) load_tile<D, BF16>(kbase, vbase, t, min(a.limit - 1, t + kTileKeys - 1), r16, grp, A);
+  if (t < a.limit)
+    load_tile<D, BF16>(kbase, vbase, t, min(a.limit - 1, t + kTileKeys - 1), r16, grp, A, fresh,
+                       knew, vnew);
 
   // ---- query rows of this lane: row = row0 + rb*16 + r16 -> candidate jq, head hq
   using QOp = QOperand<D, NR, BF16>;
@@ -432,11 +465,11 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   if constexpr (pipelined<D, NR, BF16>()) {
     // software-pipelined tile loop: two register tiles, the next one always in flight
     while (t < n) {
-      load_tile<D, BF16>(kbase, vbase, t + kStride, last, r16, grp, B);
+      load_tile<D, BF16>(kbase, vbase, t + kStride, last, r16, grp, B, fresh, knew, vnew);
       compute_tile<D, NR, BF16, RING>(A, qf, t, last, last_visible, rm, grp, scale_log2, st);
       t += kStride;
       if (t >= n) break;
-      load_tile<D, BF16>(kbase, vbase, t + kStride, last, r16, grp, A);
+      load_tile<D, BF16>(kbase, vbase, t + kStride, last, r16, grp, A, fresh, knew, vnew);
       compute_tile<D, NR, BF16, RING>(B, qf, t, last, last_visible, rm, grp, scale_log2, st);
       t += kStride;
     }
@@ -446,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
     while (t < n) {
       compute_tile<D, NR, BF16, RING>(A, qf, t, last, last_visible, rm, grp, scale_log2, st);
       t += kStride;
-      if (t < n) load_tile<D, BF16>(kbase, vbase, t, last, r16, grp, A);
+      if (t < n) load_tile<D, BF16>(kbase, vbase, t, last, r16, grp, A, fresh, knew, vnew);
     }
   }
 
@@ -962,6 +995,12 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, in
     }
     __syncthreads();
   }
+  if (a.new_k && j == 0 && hq == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    // fused draft step: every attention workgroup has finished, so the length can advance now
+    int32_t* len_p = const_cast<int32_t*>(a.seq_len);  // the caller's (mutable) lengths
+    const int32_t len = *(len_p + b);
+    len_p[b] = (len < 0 ? 0 : len) + (len < 0x7fffffff ? 1 : 0);
+  }
   if (sl == 0) {
     const float Lt = red_l[col];
     const float4 r = red_o[col];
@@ -983,16 +1022,20 @@ hipError_t launch_split(const AttnArgs& a, const SplitPlan& p, hipStream_t strea
   // row blocks beyond the register budget of (D, dtype) are never planned (rows_cap)
   constexpr int kMaxNr = BF16 ? (D == 256 ? 2 : 4) : (D == 64 ? 4 : (D == 128 ? 2 : 1));
   if (p.nr < 1 || p.nr > kMaxNr) return hipErrorInvalidValue;
-  if (ring_masked(a)) {
-    // a windowed draft step has one query token: G <= 16 rows, one row block
+  const bool ring = ring_masked(a);
+  const bool fused = a.new_k != nullptr;
+  if (ring || fused) {
+    // draft steps have one query token: G <= 16 rows, one row block
     if (p.nr != 1) return hipErrorInvalidValue;
-    attn_split_kernel<D, 1, BF16, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
+    if (ring && fused) attn_split_kernel<D, 1, BF16, true, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
+    else if (ring) attn_split_kernel<D, 1, BF16, true, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
+    else attn_split_kernel<D, 1, BF16, false, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
   } else {
     switch (p.nr) {
-      case 1: attn_split_kernel<D, 1, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
-      case 2: if constexpr (kMaxNr >= 2) attn_split_kernel<D, 2, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
-      case 3: if constexpr (kMaxNr >= 3) attn_split_kernel<D, 3, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
-      default: if constexpr (kMaxNr >= 4) attn_split_kernel<D, 4, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+      case 1: attn_split_kernel<D, 1, BF16, false, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+      case 2: if constexpr (kMaxNr >= 2) attn_split_kernel<D, 2, BF16, false, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+      case 3: if constexpr (kMaxNr >= 3) attn_split_kernel<D, 3, BF16, false, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+      default: if constexpr (kMaxNr >= 4) attn_split_kernel<D, 4, BF16, false, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
     }
   }
   return hipGetLastError();

@@ -69,6 +69,13 @@ struct AttnArgs {
   // partial results of split s of (sequence, KV head, chunk) bhc go to index
   // bhc * part_stride + part_offset + s (two launches can fill one merge: MASW working memory)
   int part_stride, part_offset;
+  // fused draft step (split kernel, one row block): append one token per sequence, then attend.
+  // new_k/new_v [batch][1][n_kv_heads][head_dim] (NULL otherwise). The split kernel reads the new
+  // token from there, workgroup (split 0, chunk 0) of each KV head copies it into its slot (and
+  // pos), and the merge kernel advances seq_len afterwards (no attention workgroup sees the bump).
+  const void* new_k;
+  const void* new_v;
+  int32_t* pos;
 };
 
 // split kernel (or cooperative kernel) writing partials, then the log-sum-exp merge over

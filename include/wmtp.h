@@ -117,6 +117,24 @@ int wmtp_ring_append(const wmtp_kv* cache, const void* k_new, const void* v_new,
 int wmtp_draft_attn_windowed(const wmtp_kv* ring, const void* q, int32_t n_q_heads, float sm_scale,
                              float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* A whole Windowed-MTP draft step in one call: exactly wmtp_ring_append(ring, k_new, v_new, 1)
+ * followed by wmtp_draft_attn_windowed(ring, q, ...) (abstract, fourth and fifth sentences: each
+ * draft step adds its token, then the draft attends sinks + window), with the same results, ring
+ * bytes, tags and seq_len. k_new/v_new are [batch][1][n_kv_heads][head_dim]. When one row block
+ * holds the query heads of a KV head (n_q_heads / n_kv_heads <= 16) it runs as two launches instead
+ * of three: the attention kernel reads the new token from k_new/v_new while storing it, and the
+ * merge advances seq_len. Workspace and errors as for wmtp_draft_attn_windowed. */
+int wmtp_draft_step_windowed(const wmtp_kv* ring, const void* k_new, const void* v_new,
+                             const void* q, int32_t n_q_heads, float sm_scale, float* out,
+                             float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* The native full-context draft step in one call: wmtp_ring_append(cache, k_new, v_new, 1) then
+ * wmtp_draft_attn_full(cache, q, ..., max_seq_len, ...); max_seq_len must bound the lengths after
+ * the append. Same fusion as wmtp_draft_step_windowed. */
+int wmtp_draft_step_full(const wmtp_kv* cache, const void* k_new, const void* v_new, const void* q,
+                         int32_t n_q_heads, float sm_scale, int32_t max_seq_len, float* out,
+                         float* lse, void* ws, size_t ws_bytes, void* stream);
+
 /* Native full-context draft step: one query token per sequence attends every cached position
  * 0..n_b-1 of a contiguous cache (window == 0), n_b = min(seq_len[b], capacity). max_seq_len is a
  * host-side upper bound on every seq_len[b] (1 <= max_seq_len <= capacity), used only to size the

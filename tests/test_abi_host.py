@@ -33,7 +33,8 @@ def test_exports_every_declared_function(lib):
                           "wmtp_verify_attn", "wmtp_attn_workspace_bytes", "wmtp_status_string",
                           "wmtp_probe_read", "wmtp_llc_flush", "wmtp_ring_rollback",
                           "wmtp_greedy_accept", "wmtp_accept_workspace_bytes",
-                          "wmtp_draft_attn_masw", "wmtp_masw_workspace_bytes"}
+                          "wmtp_draft_attn_masw", "wmtp_masw_workspace_bytes",
+                          "wmtp_draft_step_windowed", "wmtp_draft_step_full"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -212,3 +213,20 @@ def test_masw_arguments_rejected_before_launch(lib):
     assert call(hq=7) == W.WMTP_ERR_INVALID_ARG
     assert call(ws=None) == W.WMTP_ERR_WORKSPACE
     assert call(ws_bytes=need - 1) == W.WMTP_ERR_WORKSPACE
+
+
+def test_fused_steps_rejected_before_launch(lib):
+    L = W.lib()
+    win = lambda r=_kv(), kn=FAKE, vn=FAKE, ws_bytes=1 << 30: L.wmtp_draft_step_windowed(
+        ctypes.byref(r), kn, vn, FAKE, 8, 0.1, FAKE, None, FAKE, ws_bytes, None)
+    full = lambda c=_kv(**CONTIG), kn=FAKE, bound=10: L.wmtp_draft_step_full(
+        ctypes.byref(c), kn, FAKE, FAKE, 8, 0.1, bound, FAKE, None, FAKE, 1 << 30, None)
+    assert win(kn=None) == W.WMTP_ERR_INVALID_ARG
+    assert win(vn=None) == W.WMTP_ERR_INVALID_ARG
+    assert win(kn=FAKE + 4) == W.WMTP_ERR_INVALID_ARG
+    assert win(r=_kv(**CONTIG)) == W.WMTP_ERR_INVALID_ARG
+    assert win(ws_bytes=0) == W.WMTP_ERR_WORKSPACE
+    assert full(c=_kv()) == W.WMTP_ERR_INVALID_ARG
+    assert full(kn=None) == W.WMTP_ERR_INVALID_ARG
+    assert full(bound=0) == W.WMTP_ERR_INVALID_ARG
+    assert full(bound=65) == W.WMTP_ERR_INVALID_ARG

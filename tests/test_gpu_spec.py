@@ -12,7 +12,7 @@ import torch
 import oracle
 from draft_attention_amd import binding as W
 from draft_attention_amd import synth
-from gpu_common import DEV, TOL, compare, ocode, say, tdtype
+from gpu_common import DEV, append_each, compare, logical_kv, ocode, say, tdtype
 
 pytestmark = pytest.mark.gpu
 
@@ -196,3 +196,59 @@ def test_accept_feeds_rollback_on_device():
         n = int(spec.model.n[b])
         spec.seq_k[b], spec.seq_v[b] = spec.seq_k[b][:, :n], spec.seq_v[b][:, :n]
     _check_ring(spec.ring, spec.model, spec.seq_k, spec.seq_v, "after accept + rollback")
+
+
+# ------------------------------------------------------------------------------------------
+# fused draft steps: append + attend in one call == the two calls, bit for bit
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("form", ["windowed", "windowed-slack", "full"])
+@pytest.mark.parametrize("dt,d,G", [("bf16", 256, 16), ("bf16", 128, 8), ("f32", 64, 4),
+                                    ("bf16", 128, 32)])  # G = 32: several row blocks
+def test_fused_draft_step_equals_append_then_attend(form, dt, d, G):
+    B, Hkv, S, Wn, steps = 2, 2, 4, 40, 6
+    Hq = G * Hkv
+    say(f"fused draft step {form} {dt} d={d} G={G}")
+    lens = [130, 37]
+    cap = max(lens) + steps + 8
+    K, V = logical_kv(97, B, Hkv, d, max(lens) + steps, tdtype(dt))
+
+    def make():
+        if form == "full":
+            c = W.KVCache.contiguous(B, Hkv, d, cap, tdtype(dt), with_pos=True)
+        else:
+            c = W.KVCache.ring(B, Hkv, d, S, Wn, tdtype(dt), slack=3 if form == "windowed-slack" else 0)
+        append_each(c, K, V, [0] * B, lens)
+        return c
+
+    fused, split = make(), make()
+    scale = 1.0 / math.sqrt(d)
+    ws1 = W.workspace(B, Hq, Hkv, d, 1, cap)
+    ws2 = W.workspace(B, Hq, Hkv, d, 1, cap)
+    for i in range(steps):
+        kn = torch.stack([K[b, :, lens[b] + i:lens[b] + i + 1].permute(1, 0, 2) for b in range(B)]).contiguous()
+        vn = torch.stack([V[b, :, lens[b] + i:lens[b] + i + 1].permute(1, 0, 2) for b in range(B)]).contiguous()
+        q = synth.queries(98, i, B, 1, Hq, d, tdtype(dt), DEV)
+        o1 = torch.full((B, 1, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+        l1 = torch.full((B, 1, Hq), float("nan"), dtype=torch.float32, device=DEV)
+        o2, l2 = torch.full_like(o1, float("nan")), torch.full_like(l1, float("nan"))
+        W.wmtp_ring_append(split, kn, vn, 1)
+        if form == "full":
+            W.wmtp_draft_step_full(fused, kn, vn, q, Hq, scale, cap, o1, l1, ws1)
+            W.wmtp_draft_attn_full(split, q, Hq, scale, cap, o2, l2, ws2)
+        else:
+            W.wmtp_draft_step_windowed(fused, kn, vn, q, Hq, scale, o1, l1, ws1)
+            W.wmtp_draft_attn_windowed(split, q, Hq, scale, o2, l2, ws2)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"step {i}: outputs differ"
+        for name in ("k", "v", "pos", "seq_len"):
+            assert torch.equal(getattr(fused, name), getattr(split, name)), f"step {i}: {name}"
+        n = [lens[b] + i + 1 for b in range(B)]
+        kv = oracle_kv_for(K, V, dt)
+        if form == "full":
+            ro, rl = oracle.draft_full(synth.host_array(q), ocode(dt), kv, n, scale)
+        else:
+            ro, rl = oracle.draft_windowed(synth.host_array(q), ocode(dt), kv, n, S, Wn, scale)
+        compare(o1, l1, ro, rl, dt, f"fused step {i}")
+
+
+def oracle_kv_for(K, V, dt):
+    return oracle.contiguous_kv(synth.host_array(K), synth.host_array(V), ocode(dt))

@@ -267,6 +267,7 @@ def main():
             attn_only[name].append(e0.elapsed_time(e1))
     masw_res = None if args.no_composite else masw_step(
         W, synth, D3, full, ring, Hq, scale3, stream, ev, log)
+    other = None if args.no_sweep else other_workloads(W, synth, configs, stream, ev, log)
     comp = None if args.no_composite else composite(
         W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log)
     read_ceiling = read_probe(W, probe_buf, probe_out, stream, ev)
@@ -330,6 +331,7 @@ def main():
         "dropped_kv_fraction": round(1.0 - win_slots / n_mid, 5),
         "read_probe_gbs": round(read_ceiling, 1),
         "composite": comp,
+        "other_workloads": other,
         "masw": masw_res,
         "sweep": sweep_res,
         "roofline": {
@@ -464,6 +466,135 @@ def composite(W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log, iters: in
     res["note"] = ("attention-side cost of one decode iteration (eager launches); tokens per "
                    "iteration = accepted drafts a + 1; per_token_us[k][a] = iteration / (a+1); "
                    "no_speculation_step_us includes a rollback of the token it appends")
+    return res
+
+
+def other_workloads(W, synth, configs, stream, ev, log, calls: int = 100):
+    """Draft steps of the mid-context workload (L = 131072, 32q/4kv, d128, S4, W2048; windowed
+    and full, cold and warm) and of the batched ring workload (8 ragged sequences, 16q/2kv, d128,
+    S4, W2048; windowed), each a fused step (append + attend), median of `calls` calls after 20
+    warm-up calls. The appended tokens are discarded again (rollback), so every call sees the same
+    lengths."""
+    import torch
+
+    dt = torch.bfloat16
+    dev = torch.device("cuda:0")
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    res = {}
+
+    def time_calls(fn, cold):
+        """cold: each call after a 512 MiB flush, events around the call (the flush keeps the GPU
+        busy while the host queues the call, so the events bracket GPU work); p50/p10/p90.
+        warm: `calls` calls captured in one HIP graph and replayed once (back to back on the GPU,
+        no host launch gaps); mean."""
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        if not cold:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(calls):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return {"mean": round(1000.0 * e0.elapsed_time(e1) / calls, 2)}
+        pairs = []
+        for _ in range(calls):
+            W.wmtp_llc_flush(flush_buf)
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = sorted(1000.0 * a.elapsed_time(b) for a, b in pairs)
+        return {"p50": round(us[len(us) // 2], 2), "p10": round(us[len(us) // 10], 2),
+                "p90": round(us[(9 * len(us)) // 10], 2)}
+
+    # ---- mid-context draft step
+    M = configs.MID
+    L, Hq, Hkv, d, S, Wn = M.context, M.n_q_heads, M.n_kv_heads, M.head_dim, M.sink, M.window
+    cap = L + 16
+    full = W.KVCache.contiguous(1, Hkv, d, cap, dt, dev)
+    for c0 in range(0, L, 1 << 16):
+        c1 = min(L, c0 + (1 << 16))
+        full.k[0, :, c0:c1] = synth.sequence_rows(M.seed, synth.K_ID, 0, c0, c1, Hkv, d, dt, dev,
+                                                  M.k_scale)
+        full.v[0, :, c0:c1] = synth.sequence_rows(M.seed, synth.V_ID, 0, c0, c1, Hkv, d, dt, dev)
+    full.seq_len.fill_(L)
+    ring = W.KVCache.ring(1, Hkv, d, S, Wn, dt, dev, slack=1)
+    for p0, p1 in ((0, S), (L - Wn - 1, L)):
+        ring.seq_len.fill_(p0)
+        W.wmtp_ring_append(ring, full.k[0, :, p0:p1].permute(1, 0, 2).contiguous()[None],
+                           full.v[0, :, p0:p1].permute(1, 0, 2).contiguous()[None], p1 - p0)
+    kn = synth.token_rows(M.seed, synth.KNEW_ID, 0, L, L + 1, Hkv, d, dt, dev, M.k_scale)[None]
+    vn = synth.token_rows(M.seed, synth.VNEW_ID, 0, L, L + 1, Hkv, d, dt, dev)[None]
+    q = synth.queries(M.seed, 0, 1, 1, Hq, d, dt, dev)
+    out = torch.empty((1, 1, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((1, 1, Hq), dtype=torch.float32, device=dev)
+    one = torch.ones((1,), dtype=torch.int32, device=dev)
+    ws_f = W.workspace(1, Hq, Hkv, d, 1, cap, dev)
+    ws_w = W.workspace(1, Hq, Hkv, d, 1, ring.capacity, dev)
+    scale = 1.0 / math.sqrt(d)
+
+    def step_full():
+        W.wmtp_draft_step_full(full, kn, vn, q, Hq, scale, cap, out, lse, ws_f)
+        W.wmtp_ring_rollback(full, one)
+
+    def step_win():
+        W.wmtp_draft_step_windowed(ring, kn, vn, q, Hq, scale, out, lse, ws_w)
+        W.wmtp_ring_rollback(ring, one)
+
+    res["mid_context"] = {
+        "workload": M.name,
+        "full_step_us_cold": time_calls(step_full, True),
+        "windowed_step_us_cold": time_calls(step_win, True),
+        "full_step_us_warm": time_calls(step_full, False),
+        "windowed_step_us_warm": time_calls(step_win, False),
+        "note": "step = fused append + attend, then a rollback of the token (kernel ~3 us)"}
+    log(f"mid-context: full {res['mid_context']['full_step_us_cold']['p50']} us, windowed "
+        f"{res['mid_context']['windowed_step_us_cold']['p50']} us (cold p50)")
+    del full, ws_f
+
+    # ---- batched ring draft step
+    Bc = configs.BATCHED
+    B, Hq, Hkv, d, S, Wn = Bc.batch, Bc.n_q_heads, Bc.n_kv_heads, Bc.head_dim, Bc.sink, Bc.window
+    lens = [synth.uniform_int(Bc.seed, synth.LEN_ID, b, Bc.ragged_lo, Bc.context) for b in range(B)]
+    ring = W.KVCache.ring(B, Hkv, d, S, Wn, dt, dev, slack=1)
+    for b, n in enumerate(lens):  # the ring state after n appends: sinks and the last W + 1 tokens
+        sub = W.KVCache(ring.k[b:b + 1], ring.v[b:b + 1], ring.pos[b:b + 1], ring.seq_len[b:b + 1],
+                        1, Hkv, d, ring.capacity, S, Wn, ring.dtype)
+        for p0, p1 in ((0, S), (n - Wn - 1, n)):
+            sub.seq_len.fill_(p0)
+            W.wmtp_ring_append(sub, synth.token_rows(Bc.seed, synth.K_ID, b, p0, p1, Hkv, d, dt, dev)[None],
+                               synth.token_rows(Bc.seed, synth.V_ID, b, p0, p1, Hkv, d, dt, dev)[None],
+                               p1 - p0)
+    kn = torch.stack([synth.token_rows(Bc.seed, synth.KNEW_ID, b, 0, 1, Hkv, d, dt, dev)
+                      for b in range(B)])
+    vn = torch.stack([synth.token_rows(Bc.seed, synth.VNEW_ID, b, 0, 1, Hkv, d, dt, dev)
+                      for b in range(B)])
+    q = synth.queries(Bc.seed, 0, B, 1, Hq, d, dt, dev)
+    out = torch.empty((B, 1, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
+    ones = torch.ones((B,), dtype=torch.int32, device=dev)
+    ws_w = W.workspace(B, Hq, Hkv, d, 1, ring.capacity, dev)
+
+    def step_batched():
+        W.wmtp_draft_step_windowed(ring, kn, vn, q, Hq, 1.0 / math.sqrt(d), out, lse, ws_w)
+        W.wmtp_ring_rollback(ring, ones)
+
+    warm = time_calls(step_batched, False)
+    nbytes = 2 * B * (S + Wn) * Hkv * d * 2
+    res["batched"] = {"workload": Bc.name, "windowed_step_us_warm": warm,
+                      "windowed_step_us_cold": time_calls(step_batched, True),
+                      "attended_kv_bytes": nbytes,
+                      "note": "step = fused append + attend for all 8 sequences, then a rollback"}
+    log(f"batched: windowed step {warm['mean']} us (warm, graph replay)")
     return res
 
 

@@ -5,6 +5,7 @@ from device memory, and keeps no host-side state between calls, which is what ma
 capturable; replays are interleaved with unrelated eager work and synchronisations."""
 import math
 
+import numpy as np
 import pytest
 import torch
 
@@ -104,3 +105,97 @@ def test_graph_replay_matches_eager(dt):
             assert torch.equal(a, b), f"replay {r}: tensor {i} differs from the eager run"
         n = int(graphed.full.seq_len[0].item())
         assert n == L + (r + 1) * k, f"replay {r}: contiguous length {n}"
+
+
+def test_graph_replay_of_a_speculative_iteration():
+    """The whole speculative iteration as a serving engine would capture it: k fused draft steps
+    (windowed on a ring with slack, full on a contiguous cache), the target's append and
+    verification, greedy acceptance on device logits and the rollbacks driven by its device-side
+    n_drop. Replays equal the eager calls bit for bit, replay after replay."""
+    dt = torch.bfloat16
+    B, Hq, Hkv, d, S, Wn, k, V = 2, 16, 2, 128, 4, 64, 3, 512
+    L, replays = 2000, 3
+    cap = L + (replays + 2) * (k + 1) + 16
+    say(f"graph replay of a speculative iteration B={B} d={d} k={k}")
+    K, Vv = logical_kv(2201, B, Hkv, d, L, dt)
+    Kt, Vt = logical_kv(2202, B, Hkv, d, L, dt)
+    tok_k = [torch.stack([synth.token_rows(2203, synth.KNEW_ID, b, i, i + 1, Hkv, d, dt, DEV)
+                          for b in range(B)]) for i in range(k)]
+    tok_v = [torch.stack([synth.token_rows(2203, synth.VNEW_ID, b, i, i + 1, Hkv, d, dt, DEV)
+                          for b in range(B)]) for i in range(k)]
+    cand_k = torch.stack([synth.token_rows(2204, synth.KNEW_ID, b, 0, k + 1, Hkv, d, dt, DEV)
+                          for b in range(B)])
+    cand_v = torch.stack([synth.token_rows(2204, synth.VNEW_ID, b, 0, k + 1, Hkv, d, dt, DEV)
+                          for b in range(B)])
+    q3 = [synth.queries(2205, i, B, 1, Hq, d, dt, DEV) for i in range(k)]
+    q4 = synth.queries(2206, 0, B, k + 1, Hq, d, dt, DEV)
+    g0 = torch.Generator().manual_seed(7)
+    logits = torch.randn((B, k + 1, V), generator=g0).to(dt).to(DEV)
+    choice = np.argmax(logits.float().cpu().numpy(), axis=2)  # first maximum, as the rule says
+    # sequence 0 keeps its first draft, sequence 1 keeps none
+    drafts = torch.tensor([[choice[0, 0], (choice[0, 1] + 1) % V, choice[0, 2]],
+                           [(choice[1, i] + 1) % V for i in range(k)]],
+                          dtype=torch.int32, device=DEV)
+
+    class It:
+        def __init__(self):
+            self.ring = W.KVCache.ring(B, Hkv, d, S, Wn, dt, slack=k)
+            self.full = W.KVCache.contiguous(B, Hkv, d, cap, dt, with_pos=True)
+            self.tgt = W.KVCache.contiguous(B, Hkv, d, cap, dt)
+            append_all(self.ring, K, Vv, [0] * B, L)
+            append_all(self.full, K, Vv, [0] * B, L)
+            append_all(self.tgt, Kt, Vt, [0] * B, L)
+            self.ow = torch.zeros((k, B, 1, Hq, d), dtype=torch.float32, device=DEV)
+            self.lw = torch.zeros((k, B, 1, Hq), dtype=torch.float32, device=DEV)
+            self.of, self.lf = torch.zeros_like(self.ow), torch.zeros_like(self.lw)
+            self.ov = torch.zeros((B, k + 1, Hq, d), dtype=torch.float32, device=DEV)
+            self.lv = torch.zeros((B, k + 1, Hq), dtype=torch.float32, device=DEV)
+            self.choice = torch.zeros((B, k + 1), dtype=torch.int32, device=DEV)
+            self.acc, self.nxt, self.drop = (torch.zeros((B,), dtype=torch.int32, device=DEV)
+                                             for _ in range(3))
+            self.ws_w = W.workspace(B, Hq, Hkv, d, 1, self.ring.capacity)
+            self.ws_f = W.workspace(B, Hq, Hkv, d, 1, cap)
+            self.ws_v = W.workspace(B, Hq, Hkv, d, k + 1, cap)
+            self.ws_a = W.accept_workspace(B, k, V)
+
+        def run(self):
+            for i in range(k):
+                W.wmtp_draft_step_windowed(self.ring, tok_k[i], tok_v[i], q3[i], Hq, 0.09,
+                                           self.ow[i], self.lw[i], self.ws_w)
+                W.wmtp_draft_step_full(self.full, tok_k[i], tok_v[i], q3[i], Hq, 0.09, cap,
+                                       self.of[i], self.lf[i], self.ws_f)
+            W.wmtp_ring_append(self.tgt, cand_k, cand_v, k + 1)
+            W.wmtp_verify_attn(self.tgt, q4, k + 1, Hq, 0.09, cap, self.ov, self.lv, self.ws_v)
+            W.wmtp_greedy_accept(logits, k, drafts, self.choice, self.acc, self.nxt, self.drop,
+                                 self.ws_a)
+            W.wmtp_ring_rollback(self.ring, self.drop)
+            W.wmtp_ring_rollback(self.full, self.drop)
+            W.wmtp_ring_rollback(self.tgt, self.drop)
+
+        def state(self):
+            out = []
+            for c in (self.ring, self.full, self.tgt):
+                out += [c.k.clone(), c.v.clone(), c.seq_len.clone()]
+                if c.pos is not None:
+                    out.append(c.pos.clone())
+            return out + [t.clone() for t in (self.ow, self.lw, self.of, self.lf, self.ov, self.lv,
+                                              self.choice, self.acc, self.nxt, self.drop)]
+
+    eager, graphed = It(), It()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graphed.run()
+    torch.cuda.synchronize()
+    side = It()
+    for r in range(replays):
+        say(f"  replay {r}")
+        eager.run()
+        g.replay()
+        side.run()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(eager.state(), graphed.state())):
+            assert torch.equal(a, b), f"replay {r}: tensor {i} differs from the eager run"
+        assert graphed.acc.tolist() == [1, 0]
+        assert graphed.ring.seq_len.tolist() == [L + r + 1, L]
+        assert graphed.tgt.seq_len.tolist() == [L + 2 * (r + 1), L + r + 1]

@@ -365,11 +365,29 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   const int row0 = chunk * chunk_rows;
   const int row_end = min(rows, row0 + chunk_rows);
 
-  int n = a.seq_len[b];
-  n = max(n, 0);
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
   const size_t head_off = (size_t)(b * a.n_kv_heads + h) * (size_t)a.capacity * D * F::kEB;
   const char* kbase = static_cast<const char*>(a.k) + head_off;
   const char* vbase = static_cast<const char*>(a.v) + head_off;
+
+  // Tiles are dealt grid-stride: wavefront (split, wave) takes tiles (split*4 + wave) + k*(4*
+  // n_splits), so all workgroups sweep the cache together (the access pattern HBM streams best);
+  // the log-sum-exp merge does not care which keys a partial holds. The first tile is issued before
+  // anything else. Loads are clamped to row `last` and issued unconditionally once the wavefront has
+  // work (a prefetch past the end re-reads row `last` and is never used), so the compiler waits for
+  // exactly the older tile instead of draining every outstanding load. capacity <= 2^30 keeps every
+  // index below 2^31.
+  const int kStride = n_splits * kWavesPerBlock * kTileKeys;
+  int t = (split * kWavesPerBlock + wave) * kTileKeys;
+  Tile<D, BF16> A, B;
+  // The first tile is requested against the host-side bound (a.limit >= 1, so row limit-1 is
+  // always a valid address) without waiting for seq_len: the loads overlap the seq_len read, and
+  // seq_len only masks. Later tiles clamp to the last real key.
+  if (t < a.limit) load_tile<D, BF16>(kbase, vbase, t, min(a.limit - 1, t + kTileKeys - 1), r16, grp, A);
+
+  int n = a.seq_len[b];
+  n = max(n, 0);
   // fused draft step: the token at position n (its slot `fresh`) joins the attended set
   int fresh = -1;
   const char* knew = nullptr;
@@ -395,30 +413,15 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
       }
     }
     n = n < 0x7fffffff ? n + 1 : n;
+    // the first tile went out before `fresh` was known: the one wavefront whose first tile holds
+    // the new token's slot fetches that tile again, reading the token from knew/vnew
+    if (t < a.limit && fresh >= t && fresh < t + kTileKeys)
+      load_tile<D, BF16>(kbase, vbase, t, min(a.limit - 1, t + kTileKeys - 1), r16, grp, A, fresh,
+                         knew, vnew);
   }
   const RingMask rm = ring_mask(a, n);
   n = min(n, a.limit);
   const int last = n - 1;
-
-  const int r16 = lane & 15;
-  const int grp = lane >> 4;
-
-  // Tiles are dealt grid-stride: wavefront (split, wave) takes tiles (split*4 + wave) + k*(4*
-  // n_splits), so all workgroups sweep the cache together (the access pattern HBM streams best);
-  // the log-sum-exp merge does not care which keys a partial holds. The first tile is issued before
-  // anything else. Loads are clamped to row `last` and issued unconditionally once the wavefront has
-  // work (a prefetch past the end re-reads row `last` and is never used), so the compiler waits for
-  // exactly the older tile instead of draining every outstanding load. capacity <= 2^30 keeps every
-  // index below 2^31.
-  const int kStride = n_splits * kWavesPerBlock * kTileKeys;
-  int t = (split * kWavesPerBlock + wave) * kTileKeys;
-  Tile<D, BF16> A, B;
-  // The first tile is requested against the host-side bound (a.limit >= 1, so row limit-1 is
-  // always a valid address) without waiting for seq_len: the loads overlap the seq_len read, and
-  // seq_len only masks. Later tiles clamp to the last real key.
-  if (t < a.limit)
-    load_tile<D, BF16>(kbase, vbase, t, min(a.limit - 1, t + kTileKeys - 1), r16, grp, A, fresh,
-                       knew, vnew);
 
   // ---- query rows of this lane: row = row0 + rb*16 + r16 -> candidate jq, head hq
   using QOp = QOperand<D, NR, BF16>;

@@ -194,10 +194,12 @@ def main():
                 W.wmtp_draft_attn_full(full, draft_q[t], Hq, scale3, cap, out3, lse3, ws_full)
 
     def ver_phase(s: int, append: bool = True):
-        if append:
-            W.wmtp_ring_append(tgt, cand_k[s * m:(s + 1) * m][None],
-                               cand_v[s * m:(s + 1) * m][None], m)
-        W.wmtp_verify_attn(tgt, ver_q[s], m, Hq4, scale4, cap4, out4, lse4, ws_ver)
+        if append:  # the target appends the candidates and verifies them: one fused call
+            W.wmtp_verify_step(tgt, cand_k[s * m:(s + 1) * m][None],
+                               cand_v[s * m:(s + 1) * m][None], ver_q[s], m, Hq4, scale4, cap4,
+                               out4, lse4, ws_ver)
+        else:
+            W.wmtp_verify_attn(tgt, ver_q[s], m, Hq4, scale4, cap4, out4, lse4, ws_ver)
 
     phases = {"win": win_phase, "full": full_phase, "ver": ver_phase}
     if not args.graph:
@@ -420,8 +422,8 @@ def composite(W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log, iters: in
                 else:
                     W.wmtp_draft_step_full(full, tok_k[i:i + 1][None], tok_v[i:i + 1][None], q3,
                                            Hq, scale3, cap, out3, lse3, ws_full)
-            W.wmtp_ring_append(tgt, cand_k[:k + 1][None], cand_v[:k + 1][None], k + 1)
-            W.wmtp_verify_attn(tgt, q4[:, :k + 1].contiguous(), k + 1, Hq4, scale4, cap4,
+            W.wmtp_verify_step(tgt, cand_k[:k + 1][None], cand_v[:k + 1][None],
+                               q4[:, :k + 1].contiguous(), k + 1, Hq4, scale4, cap4,
                                out4[:, :k + 1], lse4[:, :k + 1], ws_ver)
             W.wmtp_greedy_accept(lg, k, dr, ch, n_acc, nxt, n_drop, ws_acc)
             W.wmtp_ring_rollback(cache, n_drop)

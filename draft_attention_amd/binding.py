@@ -66,6 +66,7 @@ def lib():
         L.wmtp_ring_rollback.argtypes = [kvp, vp, vp]
         L.wmtp_draft_step_windowed.argtypes = [kvp, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
         L.wmtp_draft_step_full.argtypes = [kvp, vp, vp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
+        L.wmtp_verify_step.argtypes = [kvp, vp, vp, vp, i32, i32, f32, i32, vp, vp, vp, sz, vp]
         L.wmtp_draft_attn_masw.argtypes = [kvp, kvp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
         L.wmtp_masw_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
         L.wmtp_masw_workspace_bytes.restype = sz
@@ -77,6 +78,7 @@ def lib():
         for name in ("wmtp_ring_append", "wmtp_draft_attn_windowed", "wmtp_draft_attn_full",
                      "wmtp_verify_attn", "wmtp_ring_rollback", "wmtp_greedy_accept",
                      "wmtp_draft_attn_masw", "wmtp_draft_step_windowed", "wmtp_draft_step_full",
+                     "wmtp_verify_step",
                      "wmtp_probe_read", "wmtp_llc_flush"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -309,6 +311,20 @@ def wmtp_draft_step_full(cache, k_new, v_new, q, n_q_heads: int, sm_scale: float
                                     int(n_q_heads), float(sm_scale), int(max_seq_len), _ptr(out),
                                     _ptr(lse), _ptr(ws), int(nbytes), _stream(stream))
     return _done(st, "wmtp_draft_step_full", check)
+
+
+def wmtp_verify_step(cache, k_new, v_new, q, m: int, n_q_heads: int, sm_scale: float,
+                     max_seq_len: int, out, lse, ws, ws_bytes: Optional[int] = None, stream=None,
+                     check=True) -> int:
+    """Append the m candidates, then verify them (one call)."""
+    _check_append(cache, k_new, v_new, m)
+    _check_attn(cache, q, m, n_q_heads, out, lse)
+    d = _desc(cache)
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    st = lib().wmtp_verify_step(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q), int(m),
+                                int(n_q_heads), float(sm_scale), int(max_seq_len), _ptr(out),
+                                _ptr(lse), _ptr(ws), int(nbytes), _stream(stream))
+    return _done(st, "wmtp_verify_step", check)
 
 
 def wmtp_draft_attn_masw(ring, slots, q, n_q_heads: int, sm_scale: float, max_slots: int, out,

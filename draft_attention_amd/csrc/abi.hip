@@ -113,13 +113,16 @@ int attention_call(const wmtp_kv* c, const void* q, int m, int n_q_heads, float 
   a.part_stride = plan.n_splits;
   a.part_offset = 0;
   if (new_k) {
-    if (plan.coop) {
-      const int st = append_call(c, new_k, new_v, 1, stream);
-      if (st != WMTP_OK) return st;
-    } else {
+    // one-launch forms: the split kernel with one new token (draft steps), the cooperative kernel
+    // on a contiguous cache (verification); anything else appends first
+    const bool fused = plan.coop ? (mode == wmtp::kModeVerify) : (m == 1);
+    if (fused) {
       a.new_k = new_k;
       a.new_v = new_v;
       a.pos = c->pos;
+    } else {
+      const int st = append_call(c, new_k, new_v, m, stream);
+      if (st != WMTP_OK) return st;
     }
   }
   hipError_t e = wmtp::launch_attention(a, plan, c->dtype, static_cast<hipStream_t>(stream));
@@ -272,6 +275,18 @@ int wmtp_draft_attn_masw(const wmtp_kv* ring, const wmtp_kv* slots, const void* 
   if (e != hipSuccess) return WMTP_ERR_HIP;
   e = wmtp::launch_merge(a, pr, total, s);
   return e == hipSuccess ? WMTP_OK : WMTP_ERR_HIP;
+}
+
+int wmtp_verify_step(const wmtp_kv* cache, const void* k_new, const void* v_new, const void* q,
+                     int32_t m, int32_t n_q_heads, float sm_scale, int32_t max_seq_len, float* out,
+                     float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_kv(cache);
+  if (st != WMTP_OK) return st;
+  if (cache->window != 0 || !k_new || !v_new) return WMTP_ERR_INVALID_ARG;
+  if (m < 1 || m > wmtp::kMaxM) return WMTP_ERR_INVALID_ARG;
+  if (max_seq_len < 1 || max_seq_len > cache->capacity) return WMTP_ERR_INVALID_ARG;
+  return attention_call(cache, q, m, n_q_heads, sm_scale, max_seq_len, wmtp::kModeVerify, out, lse,
+                        ws, ws_bytes, stream, k_new, v_new);
 }
 
 size_t wmtp_masw_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,

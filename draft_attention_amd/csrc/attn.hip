@@ -614,7 +614,7 @@ __device__ __forceinline__ int coop_slot(int key, int chunk, int tensor) {
   return key * C::kRowBytes + (chunk << 4);
 }
 
-template <int D, int NB, bool BF16, bool RING>
+template <int D, int NB, bool BF16, bool RING, bool FUSED>
 #ifndef WMTP_COOP_WPC
 #define WMTP_COOP_WPC 2
 #endif
@@ -643,12 +643,42 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
 
   int n = a.seq_len[b];
   n = max(n, 0);
+  const size_t head_off = (size_t)(b * a.n_kv_heads + h) * (size_t)a.capacity * C::kRowBytes;
+  const char* kbase = static_cast<const char*>(a.k) + head_off;
+  const char* vbase = static_cast<const char*>(a.v) + head_off;
+  // fused verification (contiguous cache): the m candidates at positions n .. n+m-1 are read from
+  // new_k/new_v ([batch][m][n_kv_heads][head_dim]) and stored by workgroup (split 0, chunk 0)
+  int fresh = 0x7fffffff;
+  const char* knew = nullptr;
+  const char* vnew = nullptr;
+  if constexpr (FUSED) {
+    fresh = n;
+    const size_t off = ((size_t)b * a.m * a.n_kv_heads + h) * C::kRowBytes;
+    knew = static_cast<const char*>(a.new_k) + off;
+    vnew = static_cast<const char*>(a.new_v) + off;
+    if (split == 0 && chunk == 0) {
+      constexpr int kPieces = C::kRowBytes / 16;
+      for (int i = tid; i < 2 * a.m * kPieces; i += kThreads) {
+        const int tensor = i / (a.m * kPieces);
+        const int j = (i / kPieces) % a.m;
+        const int c = i % kPieces;
+        const int64_t p = (int64_t)n + j;
+        if (p >= a.capacity) continue;
+        const char* src = (tensor ? vnew : knew) + (size_t)j * a.n_kv_heads * C::kRowBytes;
+        char* dst = const_cast<char*>(tensor ? vbase : kbase) + (size_t)p * C::kRowBytes;
+        reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(src)[c];
+        if (a.pos && h == 0 && tensor == 0 && c == 0) a.pos[(size_t)b * a.capacity + p] = (int32_t)p;
+      }
+    }
+    n = n <= 0x7fffffff - a.m ? n + a.m : 0x7fffffff;
+  }
   const RingMask rm = ring_mask(a, n);
   n = min(n, a.limit);
   const int last = n - 1;
   const int tiles = (n + kTileKeys - 1) / kTileKeys;
   // Addresses only depend on the host-side bound a.limit (>= 1), so the first tiles are requested
-  // without waiting for seq_len; seq_len only masks (a tile past it is computed fully masked).
+  // without waiting for seq_len (except in a fused verification); seq_len only masks (a tile past
+  // it is computed fully masked).
   const int tiles_lim = (a.limit + kTileKeys - 1) / kTileKeys;
   const int last_lim = a.limit - 1;
   const int my_tiles = split < tiles ? (tiles - split + n_splits - 1) / n_splits : 0;
@@ -658,10 +688,6 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   };
   const bool has_range = split < tiles_lim;
   const int my_stages = (my_tiles + C::kTps - 1) / C::kTps;
-
-  const size_t head_off = (size_t)(b * a.n_kv_heads + h) * (size_t)a.capacity * C::kRowBytes;
-  const char* kbase = static_cast<const char*>(a.k) + head_off;
-  const char* vbase = static_cast<const char*>(a.v) + head_off;
 
   // staging: load l of this thread is chunk q = tid + kThreads*l of the stage: tile q / (32*kChunks),
   // then K chunks before V chunks
@@ -675,7 +701,12 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
       const int key = (q / C::kChunks) % 16;
       const int c = q % C::kChunks;
       const int kg = min(tile_start(stage * C::kTps + u) + key, last_lim);
-      dst[l] = stream_load16((tensor ? vbase : kbase) + (size_t)kg * C::kRowBytes + c * 16);
+      const char* row = (tensor ? vbase : kbase) + (size_t)kg * C::kRowBytes;
+      if constexpr (FUSED) {
+        if (kg >= fresh && kg - fresh < a.m)  // a candidate of this call: row from new_k/new_v
+          row = (tensor ? vnew : knew) + (size_t)(kg - fresh) * a.n_kv_heads * C::kRowBytes;
+      }
+      dst[l] = stream_load16(row + c * 16);
     }
   };
   auto store_stage = [&](const uint4(&src)[C::kLoads], int buf) {
@@ -999,10 +1030,12 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, in
     __syncthreads();
   }
   if (a.new_k && j == 0 && hq == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-    // fused draft step: every attention workgroup has finished, so the length can advance now
+    // fused step: every attention workgroup has finished, so the length can advance now (by the
+    // m tokens the call appended)
     int32_t* len_p = const_cast<int32_t*>(a.seq_len);  // the caller's (mutable) lengths
     const int32_t len = *(len_p + b);
-    len_p[b] = (len < 0 ? 0 : len) + (len < 0x7fffffff ? 1 : 0);
+    const int32_t base = len < 0 ? 0 : len;
+    len_p[b] = base <= 0x7fffffff - a.m ? base + a.m : 0x7fffffff;
   }
   if (sl == 0) {
     const float Lt = red_l[col];
@@ -1049,33 +1082,31 @@ hipError_t launch_coop(const AttnArgs& a, const SplitPlan& p, hipStream_t stream
   dim3 grid(p.n_splits, a.batch * a.n_kv_heads * p.n_chunks);
   dim3 block(kThreads);
   const bool ring = ring_masked(a);
+  const bool fused = a.new_k != nullptr;  // fused verification: contiguous cache, one row chunk
+  if (ring && fused) return hipErrorInvalidValue;
+#define WMTP_COOP_LAUNCH(NBV)                                                                          \
+  do {                                                                                                 \
+    if (ring) attn_coop_kernel<D, NBV, BF16, true, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); \
+    else if (fused) attn_coop_kernel<D, NBV, BF16, false, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); \
+    else attn_coop_kernel<D, NBV, BF16, false, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); \
+  } while (0)
   switch (p.nr) {
     case 1:
-      if constexpr (!(BF16 && D == 64)) {
-        if (ring) attn_coop_kernel<D, 1, BF16, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
-        else attn_coop_kernel<D, 1, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
-      }
+      if constexpr (!(BF16 && D == 64)) WMTP_COOP_LAUNCH(1);
       break;
     case 2:
-      if (ring) attn_coop_kernel<D, 2, BF16, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
-      else attn_coop_kernel<D, 2, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
+      WMTP_COOP_LAUNCH(2);
       break;
     case 4:
-      if constexpr (BF16 || D != 256) {
-        if (ring) attn_coop_kernel<D, 4, BF16, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
-        else attn_coop_kernel<D, 4, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
-      }
+      if constexpr (BF16 || D != 256) WMTP_COOP_LAUNCH(4);
       break;
     case 8:
-      if constexpr (BF16 && D <= 128) {
-        if (ring) attn_coop_kernel<D, 8, BF16, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
-        else attn_coop_kernel<D, 8, BF16, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
-      } else {
-        return hipErrorInvalidValue;
-      }
+      if constexpr (BF16 && D <= 128) WMTP_COOP_LAUNCH(8);
+      else return hipErrorInvalidValue;
       break;
     default: return hipErrorInvalidValue;
   }
+#undef WMTP_COOP_LAUNCH
   return hipGetLastError();
 }
 

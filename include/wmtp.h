@@ -207,6 +207,17 @@ int wmtp_greedy_accept(const void* logits, int32_t dtype, int32_t batch, int32_t
 /* Workspace bytes of wmtp_greedy_accept (per-chunk maxima); 0 for arguments it rejects. */
 size_t wmtp_accept_workspace_bytes(int32_t batch, int32_t k, int32_t vocab);
 
+/* The target's append + verification in one call: wmtp_ring_append(cache, k_new, v_new, m) then
+ * wmtp_verify_attn(cache, q, m, ...); k_new/v_new are [batch][m][n_kv_heads][head_dim] and
+ * max_seq_len must bound the lengths after the append. When the cooperative kernel runs the
+ * verification (more than 16 query rows per KV head) it reads the candidates from k_new/v_new
+ * while storing them and the merge advances seq_len (two launches instead of three); otherwise the
+ * append runs first. Results, cache bytes and lengths equal the two calls. Errors as for
+ * wmtp_verify_attn. */
+int wmtp_verify_step(const wmtp_kv* cache, const void* k_new, const void* v_new, const void* q,
+                     int32_t m, int32_t n_q_heads, float sm_scale, int32_t max_seq_len, float* out,
+                     float* lse, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes an attention call with these sizes needs (split-K partial results). Pass
  * m = 1 for draft steps and max_seq_len = capacity for the windowed call. Depends only on its
  * arguments (not on the device). Returns 0 for arguments no attention call accepts. */

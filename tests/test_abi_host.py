@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
                           "wmtp_probe_read", "wmtp_llc_flush", "wmtp_ring_rollback",
                           "wmtp_greedy_accept", "wmtp_accept_workspace_bytes",
                           "wmtp_draft_attn_masw", "wmtp_masw_workspace_bytes",
-                          "wmtp_draft_step_windowed", "wmtp_draft_step_full"}
+                          "wmtp_draft_step_windowed", "wmtp_draft_step_full", "wmtp_verify_step"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -230,3 +230,14 @@ def test_fused_steps_rejected_before_launch(lib):
     assert full(kn=None) == W.WMTP_ERR_INVALID_ARG
     assert full(bound=0) == W.WMTP_ERR_INVALID_ARG
     assert full(bound=65) == W.WMTP_ERR_INVALID_ARG
+
+
+def test_verify_step_rejected_before_launch(lib):
+    L = W.lib()
+    call = lambda c=_kv(**CONTIG), kn=FAKE, m=4, bound=10: L.wmtp_verify_step(
+        ctypes.byref(c), kn, FAKE, FAKE, m, 8, 0.1, bound, FAKE, None, FAKE, 1 << 30, None)
+    assert call(c=_kv()) == W.WMTP_ERR_INVALID_ARG
+    assert call(kn=None) == W.WMTP_ERR_INVALID_ARG
+    assert call(m=0) == W.WMTP_ERR_INVALID_ARG
+    assert call(m=17) == W.WMTP_ERR_INVALID_ARG
+    assert call(bound=65) == W.WMTP_ERR_INVALID_ARG

@@ -252,3 +252,49 @@ def test_fused_draft_step_equals_append_then_attend(form, dt, d, G):
 
 def oracle_kv_for(K, V, dt):
     return oracle.contiguous_kv(synth.host_array(K), synth.host_array(V), ocode(dt))
+
+
+@pytest.mark.parametrize("dt,d,Hq,Hkv,m", [
+    ("bf16", 128, 32, 2, 4),    # 64 rows: cooperative kernel, fused
+    ("bf16", 128, 32, 2, 6),    # 96 rows: two row blocks per wavefront
+    ("bf16", 64, 32, 2, 5),
+    ("bf16", 256, 32, 2, 3),    # 48 rows at head_dim 256
+    ("bf16", 128, 64, 2, 3),    # 96 rows
+    ("bf16", 128, 32, 1, 8),    # 256 rows: two row chunks, both read the new rows
+    ("f32", 64, 8, 2, 6),       # 24 rows, fp32
+    ("bf16", 128, 8, 2, 2),     # 8 rows: split kernel, append first
+])
+def test_fused_verify_step_equals_append_then_verify(dt, d, Hq, Hkv, m):
+    B = 2
+    say(f"fused verify step {dt} d={d} Hq={Hq} Hkv={Hkv} m={m}")
+    lens = [3000, 517]
+    steps = 3
+    cap = max(lens) + steps * m + 24
+    K, V = logical_kv(107, B, Hkv, d, max(lens) + steps * m, tdtype(dt))
+
+    def make():
+        c = W.KVCache.contiguous(B, Hkv, d, cap, tdtype(dt), with_pos=True)
+        append_each(c, K, V, [0] * B, lens)
+        return c
+
+    fused, split = make(), make()
+    scale = 1.0 / math.sqrt(d)
+    ws1 = W.workspace(B, Hq, Hkv, d, m, cap)
+    ws2 = W.workspace(B, Hq, Hkv, d, m, cap)
+    for i in range(steps):
+        cur = [lens[b] + i * m for b in range(B)]
+        kn = torch.stack([K[b, :, cur[b]:cur[b] + m].permute(1, 0, 2) for b in range(B)]).contiguous()
+        vn = torch.stack([V[b, :, cur[b]:cur[b] + m].permute(1, 0, 2) for b in range(B)]).contiguous()
+        q = synth.queries(108, i, B, m, Hq, d, tdtype(dt), DEV)
+        o1 = torch.full((B, m, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+        l1 = torch.full((B, m, Hq), float("nan"), dtype=torch.float32, device=DEV)
+        o2, l2 = torch.full_like(o1, float("nan")), torch.full_like(l1, float("nan"))
+        W.wmtp_verify_step(fused, kn, vn, q, m, Hq, scale, cap, o1, l1, ws1)
+        W.wmtp_ring_append(split, kn, vn, m)
+        W.wmtp_verify_attn(split, q, m, Hq, scale, cap, o2, l2, ws2)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"step {i}: outputs differ"
+        for name in ("k", "v", "pos", "seq_len"):
+            assert torch.equal(getattr(fused, name), getattr(split, name)), f"step {i}: {name}"
+        n = [c + m for c in cur]
+        ro, rl = oracle.verify(synth.host_array(q), ocode(dt), oracle_kv_for(K, V, dt), n, scale)
+        compare(o1, l1, ro, rl, dt, f"fused verify step {i}")

@@ -460,9 +460,8 @@ def composite(W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log, iters: in
     ws1 = W.workspace(1, Hq4, Hkv4, d4, 1, cap4, dev)
 
     def nospec():
-        W.wmtp_ring_append(tgt, one_k, one_v, 1)
-        W.wmtp_verify_attn(tgt, q4[:, :1].contiguous(), 1, Hq4, scale4, cap4, out4[:, :1],
-                           lse4[:, :1], ws1)
+        W.wmtp_verify_step(tgt, one_k, one_v, q4[:, :1].contiguous(), 1, Hq4, scale4, cap4,
+                           out4[:, :1], lse4[:, :1], ws1)
         W.wmtp_ring_rollback(tgt, one)  # keep the cache length fixed across repetitions
     res["no_speculation_step_us"] = round(timed(nospec), 1)
     res["note"] = ("attention-side cost of one decode iteration (eager launches); tokens per "

@@ -700,11 +700,15 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
       const int tensor = (q / (16 * C::kChunks)) & 1;
       const int key = (q / C::kChunks) % 16;
       const int c = q % C::kChunks;
-      const int kg = min(tile_start(stage * C::kTps + u) + key, last_lim);
+      const int t0 = tile_start(stage * C::kTps + u);
+      const int kg = min(t0 + key, last_lim);
       const char* row = (tensor ? vbase : kbase) + (size_t)kg * C::kRowBytes;
       if constexpr (FUSED) {
-        if (kg >= fresh && kg - fresh < a.m)  // a candidate of this call: row from new_k/new_v
-          row = (tensor ? vnew : knew) + (size_t)(kg - fresh) * a.n_kv_heads * C::kRowBytes;
+        // only the last tiles can hold a candidate of this call (a workgroup-uniform test first)
+        if (t0 + kTileKeys > fresh) {
+          if (kg >= fresh && kg - fresh < a.m)  // a candidate: its row comes from new_k/new_v
+            row = (tensor ? vnew : knew) + (size_t)(kg - fresh) * a.n_kv_heads * C::kRowBytes;
+        }
       }
       dst[l] = stream_load16(row + c * 16);
     }

@@ -1,25 +1,29 @@
-// attn.hip -- split-K flash-decoding attention for gfx950 (MI355X), used by the three attention
-// entry points: the Windowed-MTP draft step (attend the occupied slots of a compact ring buffer),
+// attn.hip -- split-K flash-decoding attention for gfx950 (MI355X), used by the attention entry
+// points: the Windowed-MTP draft step (attend the sinks and recent window held by a ring buffer),
 // the native full-context draft step and the target's causal verification of m draft candidates
 // (Windowed-MTP abstract, third and fifth sentences: the native draft attends the whole KV cache;
-// the windowed draft attends sinks plus a recent window; verification stays full attention).
+// the windowed draft attends sinks plus a recent window; verification stays full attention), and
+// the MASW-style step (two reads merged into one result).
 //
-// Kernel 1 (attn_split_kernel): one workgroup of four 64-lane wavefronts owns one key range of one
-// (sequence, KV head, row chunk). The G*m query rows of a KV head form one dense operand (GQA), so
-// both products run on the matrix cores:
+// Kernel 1 (attn_split_kernel, up to 16*NR query rows per KV head): one workgroup of four 64-lane
+// wavefronts owns a share of the keys of one (sequence, KV head, row chunk). The G*m query rows of
+// a KV head form one dense operand (GQA), so both products run on the matrix cores:
 //   S^T (16 keys x 16 rows) = K_tile (16 x d) . Q^T          v_mfma_f32_16x16x32_bf16 / 16x16x4_f32
 //   O^T (16 dims x 16 rows) += V_tile^T (16 x 16 keys) . P^T  v_mfma_f32_16x16x16_bf16 / 16x16x4_f32
 // With this orientation every lane of both results holds one query row (lane & 15), so the
 // running max, running sum and the rescaling of O are per-lane scalars, and the softmax weights
 // left in the S^T registers are already the P^T operand of the second product: the inner loop uses
-// no LDS and no cross-lane traffic except two xor-shuffles for the row maximum.
+// no LDS, and cross-lane traffic only on the rare tiles that move a row's reference maximum.
 // K rows are read straight from HBM into the operand layout (16-byte loads, 64 contiguous bytes per
 // key per instruction). V rows are read with each 16-lane group streaming one key's row and are
-// transposed in registers with v_perm_b32 into the V^T operand. The four wavefronts take
-// interleaved 16-key tiles of the workgroup's range (so the workgroup streams one contiguous
-// region), and each keeps the next tile's loads in flight while it computes the current one.
-// At the end the wavefronts combine their states through LDS and wavefront 0 writes one partial
-// (o unnormalised, running max in log2 units, running sum) per query row.
+// transposed in registers with v_perm_b32 into the V^T operand. 16-key tiles are dealt grid-stride
+// over all wavefronts of the launch (all workgroups sweep the cache together), and each wavefront
+// keeps the next tile's loads in flight while it computes the current one. At the end the
+// wavefronts combine their states through LDS and wavefront 0 writes one partial (o unnormalised,
+// running max in log2 units, running sum) per query row.
+//
+// Kernel 1b (attn_coop_kernel, more rows: verification): the four wavefronts of a workgroup share
+// each tile through an LDS stage (see the comment above the kernel).
 //
 // Kernel 2 (merge_kernel): log-sum-exp merge of the partials of every output row, one workgroup per
 // (row, 32 or 64 dims):
@@ -566,10 +570,11 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
 // share of the tile (K and V rows are contiguous in HBM), keeps kPrefetch tiles of them in flight
 // in registers, and writes the oldest one into a double-buffered LDS stage (K chunks XOR-swizzled
 // by key so the operand reads below are bank-conflict free). One barrier per tile.
-// The wavefronts split the work of a tile either by query-row block (NB = 4 blocks of 16 rows, the
-// verify shape) or by output dimensions (NB = 1: each wavefront owns D/4 dims of all 16 rows and
-// recomputes the 16x16 score tile, which is cheap on the matrix cores). Each wavefront writes its
-// own part of the workgroup's partial; no cross-wavefront merge is needed.
+// The wavefronts split the work of a tile by query-row block (NB = 4: one block of 16 rows each,
+// the verify shape; NB = 8: two blocks each, sharing one V operand read) or by output dimensions
+// (NB = 1 or 2: each wavefront owns D/4 or D/2 dims of its block's rows and recomputes the 16x16
+// score tile, which is cheap on the matrix cores). Each wavefront writes its own part of the
+// workgroup's partial; no cross-wavefront merge is needed.
 template <int D, int NB, bool BF16>
 struct Coop {
   static constexpr int kEB = BF16 ? 2 : 4;

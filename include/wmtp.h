@@ -14,12 +14,20 @@
  *                                                               wmtp_verify_attn
  *   - the draft KV that is never read is reclaimed by a compact ring buffer (last sentence)
  *                                                            -> the ring layout of wmtp_kv
+ * and the steps around them in a speculative iteration:
+ *   - a draft step appends its token and attends            -> wmtp_draft_step_windowed/_full
+ *   - the target appends the candidates and verifies them   -> wmtp_verify_step
+ *   - greedy accept/reject, then discarding rejected speculative KV (MASW page, sections 1 and
+ *     4.3)                                                   -> wmtp_greedy_accept, wmtp_ring_rollback
+ *   - the MASW working memory of sinks, memory slots and a local window (MASW page, section 4.1)
+ *                                                            -> wmtp_draft_attn_masw
  *
  * Conventions (the pages fix none of them; these are the library's):
  *   - Positions: the tokens of sequence b are numbered 0, 1, 2, ... in append order; seq_len[b] is
  *     how many have been appended. Attention sinks are positions 0..sink-1; the window is the last
  *     `window` positions, the newest included; a position in both sets is attended once.
- *   - Slot map: position p lives in slot p if p < sink, else in slot sink + (p - sink) % window.
+ *   - Slot map: position p lives in slot p if p < sink, else in slot
+ *     sink + (p - sink) % (capacity - sink) (= % window for a ring without slack slots).
  *     A contiguous (non-ring) cache is the same descriptor with window = 0 and sink = capacity, so
  *     that slot(p) = p.
  *   - GQA: query head hq reads KV head hq / G, G = n_q_heads / n_kv_heads (contiguous groups).

@@ -357,6 +357,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+CPU_REPS = 3  # oracle repetitions per timed part (about 10 s of CPU work on 16 threads)
 COMPOSITE_VOCAB = 131072  # synthetic target vocabulary for the greedy acceptance step
 COMPOSITE_MARGIN = 512  # cache room for the tokens the composite keeps (a + 1 per iteration)
 
@@ -760,15 +761,17 @@ def cpu_baseline(full, tgt, ring, draft_q, ver_q, k, m, S, Wn, scale3, scale4, s
     q3 = synth.host_array(draft_q[-1])
     q4 = synth.host_array(ver_q[-1])
     log(f"cpu baseline: oracle on {threads} threads")
-    t0 = time.perf_counter()
-    oracle.draft_full(q3, oracle.BF16, kv3, [n3], scale3)
-    t_full = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.draft_windowed(q3, oracle.BF16, kv3, [n3], S, Wn, scale3)
-    t_win = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.verify(q4, oracle.BF16, kv4, [n4], scale4)
-    t_ver = time.perf_counter() - t0
+
+    def timed(fn, reps):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        return (time.perf_counter() - t0) / reps
+
+    reps = CPU_REPS
+    t_full = timed(lambda: oracle.draft_full(q3, oracle.BF16, kv3, [n3], scale3), reps)
+    t_win = timed(lambda: oracle.draft_windowed(q3, oracle.BF16, kv3, [n3], S, Wn, scale3), reps)
+    t_ver = timed(lambda: oracle.verify(q4, oracle.BF16, kv4, [n4], scale4), reps)
     t_step = k * (t_full + t_win) + t_ver
     log(f"cpu baseline: full {t_full:.2f}s windowed {t_win * 1e3:.1f}ms verify {t_ver:.2f}s")
     return {
@@ -777,8 +780,8 @@ def cpu_baseline(full, tgt, ring, draft_q, ver_q, k, m, S, Wn, scale3, scale4, s
         "cores": threads,
         "kind": "oracle",
         "sample": (f"one full-context draft step (32 heads x {n3} keys), one windowed draft step "
-                   f"and one verification (4 x 32 heads x {n4} keys), timed once each; whole "
-                   f"step = 5 x (full + windowed) + verify = {t_step:.2f} s"),
+                   f"and one verification (4 x 32 heads x {n4} keys), each timed {reps} times "
+                   f"(mean); whole step = 5 x (full + windowed) + verify = {t_step:.2f} s"),
         "draft_step_us": {"full_attn": round(t_full * 1e6, 1), "windowed_attn": round(t_win * 1e6, 1)},
         "verify_us": round(t_ver * 1e6, 1),
     }

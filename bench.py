@@ -666,11 +666,12 @@ def pct(v, q):
 
 
 def sweep(W, synth, D3, full, cap, Hq, scale, probe_buf, probe_out, stream, ev, log,
-          calls: int = 30):
+          calls: int = 100, warm_up: int = 20):
     """Single draft-step attention calls at the million-token draft shapes over a range of context
     lengths L (the step attends n = L + 1 tokens): windowed (ring holding sinks + window of the
     same sequence) and full (the first n rows of the contiguous cache), each timed per call with
-    events, cold (the caches flushed before every call) and warm (calls back to back)."""
+    events after `warm_up` calls: cold (the caches flushed before every call) and warm (calls back
+    to back behind a backlog read); median, p10 and p90 of `calls` calls."""
     import torch
 
     dev = full.k.device
@@ -704,7 +705,8 @@ def sweep(W, synth, D3, full, cap, Hq, scale, probe_buf, probe_out, stream, ev, 
             "windowed": lambda: W.wmtp_draft_attn_windowed(ring, q, Hq, scale, out, lse, ws_win),
         }
         for name, call in calls_of.items():
-            call()
+            for _ in range(warm_up):
+                call()
             cold, warm = [], []
             for _ in range(calls):
                 e0, e1 = ev(), ev()

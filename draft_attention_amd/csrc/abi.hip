@@ -31,6 +31,7 @@ int check_kv(const wmtp_kv* c) {
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return WMTP_ERR_UNSUPPORTED;
   if (!c->k || !c->v || !c->seq_len) return WMTP_ERR_INVALID_ARG;
   if (c->batch < 1 || c->n_kv_heads < 1 || c->capacity < 1) return WMTP_ERR_INVALID_ARG;
+  if (c->batch > 65535) return WMTP_ERR_INVALID_ARG;  // one grid row per sequence in the appends
   if (c->capacity > wmtp::kMaxCapacity) return WMTP_ERR_CAPACITY;
   if (c->sink < 0 || c->window < 0) return WMTP_ERR_INVALID_ARG;
   if (c->window >= 1) {

@@ -1159,6 +1159,7 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
     if (dtype == WMTP_BF16 && head_dim == 64 && p->nr < 2) p->nr = 2;
   }
   const long long bhc = (long long)batch * n_kv_heads * p->n_chunks;
+  if (bhc > 65535) return false;  // one grid row per (sequence, KV head, row chunk)
   const long long tiles_per_seq = ((long long)max_seq_len + kTileKeys - 1) / kTileKeys;
   // about target_blocks workgroups in all, but at least kMinTilesPerWave tiles per wavefront
   long long blocks = (bhc * tiles_per_seq + kWavesPerBlock * kMinTilesPerWave - 1) /

@@ -79,7 +79,10 @@ typedef enum wmtp_dtype { WMTP_F32 = 0, WMTP_BF16 = 1 } wmtp_dtype;
 
 /* A KV cache of `batch` sequences: a compact ring buffer (window >= 1, capacity >= sink + window) or
  * a contiguous cache (window = 0, sink = capacity). head_dim must be 64, 128 or 256;
- * 1 <= capacity <= 2^30 (larger capacities return WMTP_ERR_CAPACITY).
+ * 1 <= capacity <= 2^30 (larger capacities return WMTP_ERR_CAPACITY); 1 <= batch <= 65535, and an
+ * attention call needs batch * n_kv_heads * (row chunks per KV head) <= 65535, a row chunk holding
+ * 16 to 128 of a KV head's query rows (m * n_q_heads / n_kv_heads) depending on dtype and head_dim
+ * (INVALID_ARG otherwise).
  * A ring's window positions wrap over its capacity - sink window slots: slot(p) = p for p < sink,
  * else sink + (p - sink) % (capacity - sink). The draft attends the sinks and the last `window`
  * positions; the slack = capacity - sink - window extra slots let the newest `slack` tokens be

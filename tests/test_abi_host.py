@@ -241,3 +241,28 @@ def test_verify_step_rejected_before_launch(lib):
     assert call(m=0) == W.WMTP_ERR_INVALID_ARG
     assert call(m=17) == W.WMTP_ERR_INVALID_ARG
     assert call(bound=65) == W.WMTP_ERR_INVALID_ARG
+
+
+def test_grid_limits_rejected_before_launch(lib):
+    assert _append(_kv(batch=65536)) == W.WMTP_ERR_INVALID_ARG
+    # 40000 sequences x 2 KV heads = 80000 grid rows for an attention call
+    assert _windowed(_kv(batch=40000)) == W.WMTP_ERR_INVALID_ARG
+    assert W.lib().wmtp_attn_workspace_bytes(40000, 8, 2, 128, 1, 20) == 0
+
+
+@pytest.mark.parametrize("lang", ["c", "c++"])
+def test_public_headers_compile(lang, tmp_path):
+    """The headers stand alone for C and C++ callers (they declare only plain types)."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    src = tmp_path / ("use.c" if lang == "c" else "use.cpp")
+    src.write_text('#include "wmtp.h"\n#include "wmtp_probe.h"\n'
+                   'int main(void) { wmtp_kv kv; (void)kv; return wmtp_status_string(0) == 0; }\n')
+    r = subprocess.run([cc, "-fsyntax-only", "-Wall", "-Werror", "-I", inc, str(src)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr

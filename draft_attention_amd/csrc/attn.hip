@@ -598,7 +598,10 @@ struct Coop {
 #ifdef WMTP_COOP_PREFETCH
   static constexpr int kPrefetch = WMTP_COOP_PREFETCH;       // stages in flight
 #else
-  static constexpr int kPrefetch = kLoads >= 8 ? 2 : (kLoads >= 4 ? 4 : 6);
+  // stages in flight: about 16 KB per workgroup (two stages of 8 KB or more, four of 4 KB).
+  // Measured on MI355X (verification, head_dim 128, bf16, 2 workgroups per CU): 2 stages of 8 KB
+  // beat 3, 4 and 6 (more loads in flight per CU lowered the achieved bandwidth) and 1.
+  static constexpr int kPrefetch = kStageBytes >= 8192 ? 2 : 4;
 #endif
   static_assert(kLoads >= 1 && kStageBytes % (16 * kThreads) == 0, "stage must split evenly");
   static_assert(kDpl >= (BF16 ? 2 : 1), "each lane needs a pair of bf16 dims");
@@ -691,7 +694,6 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
     const int tl = split + i * n_splits;
     return (tl < tiles_lim ? tl : tiles_lim - 1) * kTileKeys;
   };
-  const bool has_range = split < tiles_lim;
   const int my_stages = (my_tiles + C::kTps - 1) / C::kTps;
 
   // staging: load l of this thread is chunk q = tid + kThreads*l of the stage: tile q / (32*kChunks),
@@ -757,9 +759,16 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   // the last key every row of the workgroup may attend (candidate 0 sees the fewest)
   const int vis_all = min(last, (a.mode == kModeVerify) ? (n - a.m) : (n - 1));
 
-  if (has_range) {
+  // The prefetch is issued on every path (a workgroup without tiles reads clamped, valid rows) and
+  // stage by stage (the scheduling barriers keep the compiler from interleaving the stages' loads):
+  // the loads outstanding at the top of the tile loop are then in the same order on entry as on
+  // the back edge, so the loop waits for exactly the oldest stage. (With a conditional prefetch,
+  // or loads grouped by index across stages, the waits merged at the loop header let only about
+  // two of the kPrefetch stages stay in flight.)
 #pragma unroll
-    for (int s = 0; s < C::kPrefetch; ++s) load_stage(stg[s], s);
+  for (int s = 0; s < C::kPrefetch; ++s) {
+    load_stage(stg[s], s);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   const float scale_log2 = a.sm_scale * kLog2e;

@@ -357,7 +357,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   __shared__ float2 sm_ml[kWavesPerBlock - 1][kRows];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // the wavefront index is uniform across the wavefront: in a scalar register, tile indices and
+  // loop conditions derived from it stay scalar (uniform branches instead of exec-mask loops,
+  // whose merged paths made the compiler wait for most of a tile before requesting the next)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x;
   const int bhc = blockIdx.y;
   const int chunk = bhc % n_chunks;
@@ -375,20 +378,57 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   const char* kbase = static_cast<const char*>(a.k) + head_off;
   const char* vbase = static_cast<const char*>(a.v) + head_off;
 
+  // ---- query rows of this lane: row = row0 + rb*16 + r16 -> candidate jq, head hq. The query
+  // loads go out first, ahead of the first tile: every later wait for a tile then also covers
+  // them, on the first pass through the tile loop as on the others.
+  using QOp = QOperand<D, NR, BF16>;
+  static_assert(!QOp::kInLds || NR <= kWavesPerBlock, "one row block per wavefront for the LDS copy");
+  __shared__ uint4 sm_q[QOp::kInLds ? NR * F::kQRegs * 64 : 1];
+  int row_j[NR];  // candidate index of the row
+  bool row_ok[NR];
+  QOp qf;
+  qf.lds = sm_q;
+  qf.lane = lane;
+  uint4 qraw[QOp::kInLds ? F::kQRegs : 1];  // LDS copy: this wavefront's row block, stored later
+#pragma unroll
+  for (int rb = 0; rb < NR; ++rb) {
+    const int row = row0 + rb * 16 + r16;
+    row_ok[rb] = row < row_end;
+    // padding rows load the last real row (never written out; no select, so no early wait)
+    const int row_q = row_ok[rb] ? row : row_end - 1;
+    const int jq = row_q / G;
+    const int hq = h * G + row_q % G;
+    row_j[rb] = jq;
+    if (QOp::kInLds && rb != wave) continue;  // LDS copy: one wave per row block
+    const size_t qoff = ((size_t)(b * a.m + jq) * a.n_q_heads + hq) * D;
+#pragma unroll
+    for (int ks = 0; ks < F::kQRegs; ++ks) {
+      // bf16: dims ks*32 + grp*8 .. +7; fp32: dims ks*16 + grp*4 .. +3 (the chunk K holds)
+      const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
+                                                        qoff * F::kEB + (ks * 4 + grp) * 16);
+      if constexpr (QOp::kInLds)
+        qraw[ks] = raw;
+      else
+        qf.reg[rb][ks] = __builtin_bit_cast(typename QOp::Vec, raw);
+    }
+  }
+
   // Tiles are dealt grid-stride: wavefront (split, wave) takes tiles (split*4 + wave) + k*(4*
   // n_splits), so all workgroups sweep the cache together (the access pattern HBM streams best);
-  // the log-sum-exp merge does not care which keys a partial holds. The first tile is issued before
-  // anything else. Loads are clamped to row `last` and issued unconditionally once the wavefront has
-  // work (a prefetch past the end re-reads row `last` and is never used), so the compiler waits for
-  // exactly the older tile instead of draining every outstanding load. capacity <= 2^30 keeps every
-  // index below 2^31.
+  // the log-sum-exp merge does not care which keys a partial holds. Loads are clamped to row
+  // `last` and issued unconditionally (a prefetch past the end re-reads row `last` and is never
+  // used), so the compiler waits for exactly the older tile instead of draining every outstanding
+  // load. capacity <= 2^30 and kStride <= 64 * (the planner's workgroup target, 256) keep every
+  // index, t + 2 * kStride included, below 2^31.
   const int kStride = n_splits * kWavesPerBlock * kTileKeys;
   int t = (split * kWavesPerBlock + wave) * kTileKeys;
   Tile<D, BF16> A, B;
   // The first tile is requested against the host-side bound (a.limit >= 1, so row limit-1 is
   // always a valid address) without waiting for seq_len: the loads overlap the seq_len read, and
-  // seq_len only masks. Later tiles clamp to the last real key.
-  if (t < a.limit) load_tile<D, BF16>(kbase, vbase, t, min(a.limit - 1, t + kTileKeys - 1), r16, grp, A);
+  // seq_len only masks. Later tiles clamp to the last real key. (A wavefront without tiles reads
+  // row limit-1; the request is unconditional so that every path into the tile loop has the same
+  // loads outstanding.)
+  load_tile<D, BF16>(kbase, vbase, t, min(a.limit - 1, t + kTileKeys - 1), r16, grp, A);
 
   int n = a.seq_len[b];
   n = max(n, 0);
@@ -427,37 +467,17 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   n = min(n, a.limit);
   const int last = n - 1;
 
-  // ---- query rows of this lane: row = row0 + rb*16 + r16 -> candidate jq, head hq
-  using QOp = QOperand<D, NR, BF16>;
-  __shared__ uint4 sm_q[QOp::kInLds ? NR * F::kQRegs * 64 : 1];
   int last_visible[NR];  // largest key index the row may attend
-  bool row_ok[NR];
-  QOp qf;
-  qf.lds = sm_q;
-  qf.lane = lane;
 #pragma unroll
-  for (int rb = 0; rb < NR; ++rb) {
-    const int row = row0 + rb * 16 + r16;
-    row_ok[rb] = row < row_end;
-    // padding rows load the last real row (never written out; no select, so no early wait)
-    const int row_q = row_ok[rb] ? row : row_end - 1;
-    const int jq = row_q / G;
-    const int hq = h * G + row_q % G;
-    last_visible[rb] = (a.mode == kModeVerify) ? (n - a.m + jq) : (n - 1);
-    if (QOp::kInLds && rb % kWavesPerBlock != wave) continue;  // LDS copy: one wave per row block
-    const size_t qoff = ((size_t)(b * a.m + jq) * a.n_q_heads + hq) * D;
+  for (int rb = 0; rb < NR; ++rb)
+    last_visible[rb] = (a.mode == kModeVerify) ? (n - a.m + row_j[rb]) : (n - 1);
+  if constexpr (QOp::kInLds) {
+    if (wave < NR) {
 #pragma unroll
-    for (int ks = 0; ks < F::kQRegs; ++ks) {
-      // bf16: dims ks*32 + grp*8 .. +7; fp32: dims ks*16 + grp*4 .. +3 (the chunk K holds)
-      const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
-                                                        qoff * F::kEB + (ks * 4 + grp) * 16);
-      if constexpr (QOp::kInLds)
-        sm_q[(rb * F::kQRegs + ks) * 64 + lane] = raw;
-      else
-        qf.reg[rb][ks] = __builtin_bit_cast(typename QOp::Vec, raw);
+      for (int ks = 0; ks < F::kQRegs; ++ks) sm_q[(wave * F::kQRegs + ks) * 64 + lane] = qraw[ks];
     }
+    __syncthreads();
   }
-  if constexpr (QOp::kInLds) __syncthreads();
 
   const float scale_log2 = a.sm_scale * kLog2e;
   RowState<D, NR, BF16> st;
@@ -470,15 +490,28 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   }
 
   if constexpr (pipelined<D, NR, BF16>()) {
-    // software-pipelined tile loop: two register tiles, the next one always in flight
+    // software-pipelined tile loop: two register tiles, the next one always in flight. A round
+    // takes two tiles and has no exit in its middle: the second tile's successor is requested
+    // (clamped) even when the second tile is past the end and is not computed. Every path then
+    // reaches each tile's first use with the same loads issued after it, so the compiler waits for
+    // exactly that tile (an exit inside the round, or a conditional request, made it wait for most
+    // of a tile before requesting the next). The scheduling barriers keep each request ahead of
+    // the computation it overlaps.
+    if (t < n && t + kStride >= n) {
+      // a single tile (the windowed read's usual share): nothing to overlap
+      compute_tile<D, NR, BF16, RING>(A, qf, t, last, last_visible, rm, grp, scale_log2, st);
+      t = n;
+    }
     while (t < n) {
       load_tile<D, BF16>(kbase, vbase, t + kStride, last, r16, grp, B, fresh, knew, vnew);
+      __builtin_amdgcn_sched_barrier(0);
       compute_tile<D, NR, BF16, RING>(A, qf, t, last, last_visible, rm, grp, scale_log2, st);
-      t += kStride;
-      if (t >= n) break;
-      load_tile<D, BF16>(kbase, vbase, t + kStride, last, r16, grp, A, fresh, knew, vnew);
-      compute_tile<D, NR, BF16, RING>(B, qf, t, last, last_visible, rm, grp, scale_log2, st);
-      t += kStride;
+      load_tile<D, BF16>(kbase, vbase, t + 2 * kStride, last, r16, grp, A, fresh, knew, vnew);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + kStride < n)
+        compute_tile<D, NR, BF16, RING>(B, qf, t + kStride, last, last_visible, rm, grp, scale_log2,
+                                        st);
+      t += 2 * kStride;
     }
   } else {
     // one register tile: loads of tile t + stride start once tile t is consumed

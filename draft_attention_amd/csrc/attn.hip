@@ -995,8 +995,9 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
 // One workgroup per (output row, 4*COLS dims). COLS threads cover the dims as float4 columns;
 // 256/COLS lanes of splits stride over the partials in one online pass (each lane keeps its own
 // running max and rescales), a batch of COLS independent loads per lane covering 256 splits; the
-// lanes then combine through LDS with the same rescaling rule. Measured on MI355X: 8 columns are
-// faster for the draft steps' 65-128 splits per row, 16 for verification's 256.
+// lanes then combine with the same rescaling rule, by shuffles inside each wavefront and through
+// LDS across the four. Measured on MI355X: 8 columns are faster for the draft steps' 65-128 splits
+// per row, 16 for verification's 256.
 template <int D, int COLS>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, int n_chunks,
                                                     int chunk_rows, int nr) {
@@ -1061,24 +1062,37 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, in
       if (s0 + i * kSplitLanes < n_splits) absorb(ml[i], x[i]);
   }
 
-  red_m[tid] = M;
-  red_l[tid] = L;
-  red_o[tid] = acc;
+  // combine (M, L, acc) over the split lanes: first inside the wavefront (lanes that differ in
+  // the split bits of the lane index, by cross-lane shuffles), then the four wavefronts' results
+  // through LDS with one barrier
+  auto combine = [&](float m2, float l2, float4 x2) {
+    const float mm = fmaxf(M, m2);
+    const float mu = (mm == -INFINITY) ? 0.f : mm;
+    const float c1 = __builtin_amdgcn_exp2f(M - mu), c2 = __builtin_amdgcn_exp2f(m2 - mu);
+    M = mm;
+    L = c1 * L + c2 * l2;
+    acc = make_float4(c1 * acc.x + c2 * x2.x, c1 * acc.y + c2 * x2.y, c1 * acc.z + c2 * x2.z,
+                      c1 * acc.w + c2 * x2.w);
+  };
+#pragma unroll
+  for (int off = kCols; off < 64; off <<= 1)
+    combine(__shfl_xor(M, off), __shfl_xor(L, off),
+            make_float4(__shfl_xor(acc.x, off), __shfl_xor(acc.y, off), __shfl_xor(acc.z, off),
+                        __shfl_xor(acc.w, off)));
+  const int wave = tid >> 6;
+  if ((tid & 63) < kCols) {
+    red_m[wave * kCols + col] = M;
+    red_l[wave * kCols + col] = L;
+    red_o[wave * kCols + col] = acc;
+  }
   __syncthreads();
-  for (int off = kSplitLanes / 2; off > 0; off >>= 1) {
-    if (sl < off) {
-      const int o2 = tid + off * kCols;
-      const float m1 = red_m[tid], m2 = red_m[o2];
-      const float mm = fmaxf(m1, m2);
-      const float mu = (mm == -INFINITY) ? 0.f : mm;
-      const float c1 = __builtin_amdgcn_exp2f(m1 - mu), c2 = __builtin_amdgcn_exp2f(m2 - mu);
-      const float4 x1 = red_o[tid], x2 = red_o[o2];
-      red_m[tid] = mm;
-      red_l[tid] = c1 * red_l[tid] + c2 * red_l[o2];
-      red_o[tid] = make_float4(c1 * x1.x + c2 * x2.x, c1 * x1.y + c2 * x2.y, c1 * x1.z + c2 * x2.z,
-                               c1 * x1.w + c2 * x2.w);
-    }
-    __syncthreads();
+  if (sl == 0) {
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+      combine(red_m[w * kCols + col], red_l[w * kCols + col], red_o[w * kCols + col]);
+    red_m[col] = M;
+    red_l[col] = L;
+    red_o[col] = acc;
   }
   if (a.new_k && j == 0 && hq == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
     // fused step: every attention workgroup has finished, so the length can advance now (by the

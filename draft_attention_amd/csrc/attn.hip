@@ -996,8 +996,9 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
 // 256/COLS lanes of splits stride over the partials in one online pass (each lane keeps its own
 // running max and rescales), a batch of COLS independent loads per lane covering 256 splits; the
 // lanes then combine with the same rescaling rule, by shuffles inside each wavefront and through
-// LDS across the four. Measured on MI355X: 8 columns are faster for the draft steps' 65-128 splits
-// per row, 16 for verification's 256.
+// LDS across the four. Measured on MI355X: 8 columns (twice the workgroups, half the loads per
+// lane) are as fast or faster up to 256 splits per row (the draft steps' 65-128, verification's
+// 256); 16 columns take larger split counts in one batch.
 template <int D, int COLS>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, int n_chunks,
                                                     int chunk_rows, int nr) {
@@ -1235,7 +1236,7 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
 template <int D>
 hipError_t launch_merge(const AttnArgs& a, const SplitPlan& p, int total_splits, hipStream_t stream) {
   const unsigned rows = a.batch * a.m * a.n_q_heads;
-  if (total_splits > 128)
+  if (total_splits > 256)
     merge_kernel<D, 16><<<dim3(rows, D / 64), dim3(256), 0, stream>>>(a, total_splits, p.n_chunks,
                                                                      p.chunk_rows, p.nr);
   else

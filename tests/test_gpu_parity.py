@@ -198,6 +198,27 @@ def test_verify_parity(dt, d, Hq, Hkv, m, lens):
     compare(out, lse, ref_o, ref_l, dt, "verify")
 
 
+@pytest.mark.parametrize("m,Hq", [(1, 8), (4, 32)])
+def test_loose_host_bound(m, Hq):
+    """A host bound far above every length sizes the launch for 64K keys: most workgroups then
+    have no tile of a short sequence (they request clamped rows and contribute nothing)."""
+    dt, d, Hkv, lens, bound = "bf16", 128, 2, [300, 4100], 65536
+    B = len(lens)
+    say(f"loose host bound {bound}: m={m} Hq={Hq} lens={lens}")
+    K, V = logical_kv(45, B, Hkv, d, max(lens), tdtype(dt))
+    cache = W.KVCache.contiguous(B, Hkv, d, bound + 16, tdtype(dt))
+    append_each(cache, K, V, [0] * B, lens)
+    q = synth.queries(46, 0, B, m, Hq, d, tdtype(dt), DEV)
+    if m == 1:
+        out, lse = run_full(cache, q, Hq, 0.1, bound)
+        ref_o, ref_l = oracle.draft_full(synth.host_array(q), ocode(dt), oracle_kv(K, V, dt), lens,
+                                         0.1)
+    else:
+        out, lse = run_verify(cache, q, Hq, 0.1, bound)
+        ref_o, ref_l = oracle.verify(synth.host_array(q), ocode(dt), oracle_kv(K, V, dt), lens, 0.1)
+    compare(out, lse, ref_o, ref_l, dt, "loose host bound")
+
+
 # ------------------------------------------------------------------------------------------
 # properties that hold on the device
 # ------------------------------------------------------------------------------------------

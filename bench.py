@@ -109,8 +109,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the hot path "
-              "has no multi-GPU form", file=sys.stderr)
+        print(f"bench.py: the attention path runs on one GPU (got --gpus {args.gpus}); it has no "
+              "multi-GPU form", file=sys.stderr)
         sys.exit(2)
 
     import torch

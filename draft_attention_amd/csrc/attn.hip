@@ -353,8 +353,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   using F = Frag<D, BF16>;
   constexpr int kRows = 16 * NR;
   constexpr int kPitch = D + 4;  // LDS row pitch (floats): rows start 4 banks apart
-  __shared__ float sm_o[kWavesPerBlock - 1][kRows * kPitch];
-  __shared__ float2 sm_ml[kWavesPerBlock - 1][kRows];
+  __shared__ float sm_o[kWavesPerBlock][kRows * kPitch];
+  __shared__ float2 sm_ml[kWavesPerBlock][kRows];
 
   const int lane = threadIdx.x & 63;
   // the wavefront index is uniform across the wavefront: in a scalar register, tile indices and
@@ -527,73 +527,62 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
 #pragma unroll
   for (int rb = 0; rb < NR; ++rb) l_row[rb] = xgroup_sum(st.l[rb]);
 
-  // ---- combine the four wavefronts' states through LDS
-  if (wave > 0) {
-#pragma unroll
-    for (int rb = 0; rb < NR; ++rb) {
-      const int rloc = rb * 16 + r16;
-      float* dst = &sm_o[wave - 1][rloc * kPitch];
-#pragma unroll
-      for (int sx = 0; sx < F::kSets; ++sx)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int u = 0; u < F::kDpl; u += 4)
-            *reinterpret_cast<float4*>(dst + out_dim<D, BF16>(sx, grp, j) + u) =
-                make_float4(st.o[rb][sx * F::kDpl + u][j], st.o[rb][sx * F::kDpl + u + 1][j],
-                            st.o[rb][sx * F::kDpl + u + 2][j], st.o[rb][sx * F::kDpl + u + 3][j]);
-      if (grp == 0) sm_ml[wave - 1][rloc] = make_float2(st.m[rb], l_row[rb]);
-    }
-  }
-  __syncthreads();
-  if (wave != 0) return;
-
-  const size_t part = (size_t)bhc * a.part_stride + a.part_offset + split;
+  // ---- combine the four wavefronts' states through LDS: every wavefront stores its state, then
+  // wavefront w combines dims [w*D/4, (w+1)*D/4) of every row of the workgroup and writes that
+  // part of the partial (the four share the combining work and the stores)
 #pragma unroll
   for (int rb = 0; rb < NR; ++rb) {
     const int rloc = rb * 16 + r16;
-    float mw[kWavesPerBlock], lw[kWavesPerBlock];
-    mw[0] = st.m[rb];
-    lw[0] = l_row[rb];
-    float M = mw[0];
-#pragma unroll
-    for (int x = 1; x < kWavesPerBlock; ++x) {
-      const float2 ml = sm_ml[x - 1][rloc];
-      mw[x] = ml.x;
-      lw[x] = ml.y;
-      M = fmaxf(M, ml.x);
-    }
-    const float m_use = (M == -INFINITY) ? 0.f : M;
-    float wgt[kWavesPerBlock];
-    float L = 0.f;
-#pragma unroll
-    for (int x = 0; x < kWavesPerBlock; ++x) {
-      wgt[x] = __builtin_amdgcn_exp2f(mw[x] - m_use);
-      L += wgt[x] * lw[x];
-    }
-    if (!row_ok[rb]) continue;
-    float* dst = a.ws_o + (part * kRows + rloc) * D;
+    float* dst = &sm_o[wave][rloc * kPitch];
 #pragma unroll
     for (int sx = 0; sx < F::kSets; ++sx)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int u = 0; u < F::kDpl; u += 4) {
-          const int dim = out_dim<D, BF16>(sx, grp, j) + u;
-          float4 acc = make_float4(wgt[0] * st.o[rb][sx * F::kDpl + u][j],
-                                   wgt[0] * st.o[rb][sx * F::kDpl + u + 1][j],
-                                   wgt[0] * st.o[rb][sx * F::kDpl + u + 2][j],
-                                   wgt[0] * st.o[rb][sx * F::kDpl + u + 3][j]);
+        for (int u = 0; u < F::kDpl; u += 4)
+          *reinterpret_cast<float4*>(dst + out_dim<D, BF16>(sx, grp, j) + u) =
+              make_float4(st.o[rb][sx * F::kDpl + u][j], st.o[rb][sx * F::kDpl + u + 1][j],
+                          st.o[rb][sx * F::kDpl + u + 2][j], st.o[rb][sx * F::kDpl + u + 3][j]);
+    if (grp == 0) sm_ml[wave][rloc] = make_float2(st.m[rb], l_row[rb]);
+  }
+  __syncthreads();
+
+  const size_t part = (size_t)bhc * a.part_stride + a.part_offset + split;
+  constexpr int kQuarter = D / kWavesPerBlock;  // dims combined by one wavefront
+  constexpr int kF4 = kQuarter / 4;             // their float4 columns per row
+  static_assert((16 * kF4) % 64 == 0, "a row block's quarter spreads evenly over the lanes");
 #pragma unroll
-          for (int x = 1; x < kWavesPerBlock; ++x) {
-            const float4 y = *reinterpret_cast<const float4*>(&sm_o[x - 1][rloc * kPitch + dim]);
-            acc.x += wgt[x] * y.x; acc.y += wgt[x] * y.y;
-            acc.z += wgt[x] * y.z; acc.w += wgt[x] * y.w;
-          }
-          *reinterpret_cast<float4*>(dst + dim) = acc;
-        }
-    if (grp == 0)
-      *reinterpret_cast<float2*>(a.ws_ml + (part * kRows + rloc) * 2) = make_float2(M, L);
+  for (int rb = 0; rb < NR; ++rb) {
+#pragma unroll
+    for (int it = 0; it < 16 * kF4 / 64; ++it) {
+      const int item = lane + 64 * it;
+      const int rloc = rb * 16 + item / kF4;
+      const int dim = wave * kQuarter + 4 * (item % kF4);
+      float mw[kWavesPerBlock], lw[kWavesPerBlock];
+      float M = -INFINITY;
+#pragma unroll
+      for (int x = 0; x < kWavesPerBlock; ++x) {
+        const float2 ml = sm_ml[x][rloc];
+        mw[x] = ml.x;
+        lw[x] = ml.y;
+        M = fmaxf(M, ml.x);
+      }
+      const float m_use = (M == -INFINITY) ? 0.f : M;
+      float L = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int x = 0; x < kWavesPerBlock; ++x) {
+        const float wgt = __builtin_amdgcn_exp2f(mw[x] - m_use);
+        L += wgt * lw[x];
+        const float4 y = *reinterpret_cast<const float4*>(&sm_o[x][rloc * kPitch + dim]);
+        acc.x += wgt * y.x; acc.y += wgt * y.y;
+        acc.z += wgt * y.z; acc.w += wgt * y.w;
+      }
+      if (row0 + rloc >= row_end) continue;  // padding row
+      *reinterpret_cast<float4*>(a.ws_o + (part * kRows + rloc) * D + dim) = acc;
+      if (wave == 0 && item % kF4 == 0)
+        *reinterpret_cast<float2*>(a.ws_ml + (part * kRows + rloc) * 2) = make_float2(M, L);
+    }
   }
 }
 

@@ -52,6 +52,20 @@ __device__ __forceinline__ uint2 stream_load8(const void* p) {
   return __builtin_bit_cast(uint2, __builtin_nontemporal_load(static_cast<const u32x2_t*>(p)));
 }
 
+// Requests every kernel argument in one round of scalar loads. Left alone, the compiler loads the
+// fields in the order the code first needs them, waiting between rounds: two or three dependent
+// round trips to the kernel-argument segment before the first vector load. Used by the merge
+// (a few microseconds in all) and the cooperative kernel; measured on MI355X, the split kernel
+// (whose first rounds overlap its integer set-up) is as fast or faster without it.
+__device__ __forceinline__ void request_args(const AttnArgs& a) {
+  asm volatile("" ::"s"(a.q), "s"(a.k), "s"(a.v), "s"(a.seq_len), "s"(a.out), "s"(a.lse),
+               "s"(a.ws_o), "s"(a.ws_ml), "s"(a.batch), "s"(a.n_kv_heads), "s"(a.n_q_heads),
+               "s"(a.m), "s"(a.capacity), "s"(a.limit), "s"(a.mode), "s"(a.sm_scale), "s"(a.sink),
+               "s"(a.window), "s"(a.wphys), "s"(a.part_stride), "s"(a.part_offset), "s"(a.new_k),
+               "s"(a.new_v), "s"(a.pos));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.f;  // softmax weights stay below 2^8 between rescales
@@ -653,6 +667,7 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   using C = Coop<D, NB, BF16>;
   typedef typename std::conditional<BF16, bf16x8_t, f32x4_t>::type QVec;
   __shared__ __attribute__((aligned(16))) char sm_tile[2][C::kStageBytes];
+  request_args(a);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -671,52 +686,57 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   const int r16 = lane & 15;
   const int grp = lane >> 4;
 
-  int n = a.seq_len[b];
-  n = max(n, 0);
   const size_t head_off = (size_t)(b * a.n_kv_heads + h) * (size_t)a.capacity * C::kRowBytes;
   const char* kbase = static_cast<const char*>(a.k) + head_off;
   const char* vbase = static_cast<const char*>(a.v) + head_off;
+
+  // query operand of this wavefront's row block. Loaded before the tile prefetch so that the
+  // loads outstanding at the top of the tile loop are the same on entry and on the back edge
+  // (otherwise the compiler drains every load there, once per round of kPrefetch tiles).
+  // A padding row (past the last query row) loads the last real row instead of zeros: its
+  // results are never written, and an unconditional load needs no wait before the prefetch.
+  bool row_ok[C::kRbw];
+  int row_j[C::kRbw];  // candidate index of the row
+  QVec qf[C::kRbw][C::kQRegs];
+#pragma unroll
+  for (int j = 0; j < C::kRbw; ++j) {
+    const int row = chunk * chunk_rows + (rb0 + kWavesPerBlock * j) * 16 + r16;
+    row_ok[j] = row < row_end;
+    const int row_q = row_ok[j] ? row : row_end - 1;
+    const int jq = row_q / G;
+    const int hq = h * G + row_q % G;
+    row_j[j] = jq;
+    const size_t qoff = ((size_t)(b * a.m + jq) * a.n_q_heads + hq) * D;
+#pragma unroll
+    for (int ks = 0; ks < C::kQRegs; ++ks)
+      qf[j][ks] = __builtin_bit_cast(
+          QVec, *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + qoff * C::kEB +
+                                                (ks * 4 + grp) * 16));
+  }
+  // seq_len: read before the tile prefetch in a fused verification (the candidates' positions
+  // steer its loads), else only once the prefetch is out (it only masks)
+  int n = 0;
   // fused verification (contiguous cache): the m candidates at positions n .. n+m-1 are read from
   // new_k/new_v ([batch][m][n_kv_heads][head_dim]) and stored by workgroup (split 0, chunk 0)
   int fresh = 0x7fffffff;
   const char* knew = nullptr;
   const char* vnew = nullptr;
   if constexpr (FUSED) {
+    n = max(a.seq_len[b], 0);
     fresh = n;
     const size_t off = ((size_t)b * a.m * a.n_kv_heads + h) * C::kRowBytes;
     knew = static_cast<const char*>(a.new_k) + off;
     vnew = static_cast<const char*>(a.new_v) + off;
-    if (split == 0 && chunk == 0) {
-      constexpr int kPieces = C::kRowBytes / 16;
-      for (int i = tid; i < 2 * a.m * kPieces; i += kThreads) {
-        const int tensor = i / (a.m * kPieces);
-        const int j = (i / kPieces) % a.m;
-        const int c = i % kPieces;
-        const int64_t p = (int64_t)n + j;
-        if (p >= a.capacity) continue;
-        const char* src = (tensor ? vnew : knew) + (size_t)j * a.n_kv_heads * C::kRowBytes;
-        char* dst = const_cast<char*>(tensor ? vbase : kbase) + (size_t)p * C::kRowBytes;
-        reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(src)[c];
-        if (a.pos && h == 0 && tensor == 0 && c == 0) a.pos[(size_t)b * a.capacity + p] = (int32_t)p;
-      }
-    }
-    n = n <= 0x7fffffff - a.m ? n + a.m : 0x7fffffff;
   }
-  const RingMask rm = ring_mask(a, n);
-  n = min(n, a.limit);
-  const int last = n - 1;
-  const int tiles = (n + kTileKeys - 1) / kTileKeys;
   // Addresses only depend on the host-side bound a.limit (>= 1), so the first tiles are requested
   // without waiting for seq_len (except in a fused verification); seq_len only masks (a tile past
   // it is computed fully masked).
   const int tiles_lim = (a.limit + kTileKeys - 1) / kTileKeys;
   const int last_lim = a.limit - 1;
-  const int my_tiles = split < tiles ? (tiles - split + n_splits - 1) / n_splits : 0;
   auto tile_start = [&](int i) {  // first key of the workgroup's i-th tile, clamped into range
     const int tl = split + i * n_splits;
     return (tl < tiles_lim ? tl : tiles_lim - 1) * kTileKeys;
   };
-  const int my_stages = (my_tiles + C::kTps - 1) / C::kTps;
 
   // staging: load l of this thread is chunk q = tid + kThreads*l of the stage: tile q / (32*kChunks),
   // then K chunks before V chunks
@@ -755,32 +775,6 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
     }
   };
 
-  // query operand of this wavefront's row block. Loaded before the tile prefetch so that the
-  // loads outstanding at the top of the tile loop are the same on entry and on the back edge
-  // (otherwise the compiler drains every load there, once per round of kPrefetch tiles).
-  // A padding row (past the last query row) loads the last real row instead of zeros: its
-  // results are never written, and an unconditional load needs no wait before the prefetch.
-  bool row_ok[C::kRbw];
-  int last_visible[C::kRbw];
-  QVec qf[C::kRbw][C::kQRegs];
-#pragma unroll
-  for (int j = 0; j < C::kRbw; ++j) {
-    const int row = chunk * chunk_rows + (rb0 + kWavesPerBlock * j) * 16 + r16;
-    row_ok[j] = row < row_end;
-    const int row_q = row_ok[j] ? row : row_end - 1;
-    const int jq = row_q / G;
-    const int hq = h * G + row_q % G;
-    last_visible[j] = (a.mode == kModeVerify) ? (n - a.m + jq) : (n - 1);
-    const size_t qoff = ((size_t)(b * a.m + jq) * a.n_q_heads + hq) * D;
-#pragma unroll
-    for (int ks = 0; ks < C::kQRegs; ++ks)
-      qf[j][ks] = __builtin_bit_cast(
-          QVec, *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + qoff * C::kEB +
-                                                (ks * 4 + grp) * 16));
-  }
-  // the last key every row of the workgroup may attend (candidate 0 sees the fewest)
-  const int vis_all = min(last, (a.mode == kModeVerify) ? (n - a.m) : (n - 1));
-
   // The prefetch is issued on every path (a workgroup without tiles reads clamped, valid rows) and
   // stage by stage (the scheduling barriers keep the compiler from interleaving the stages' loads):
   // the loads outstanding at the top of the tile loop are then in the same order on entry as on
@@ -792,6 +786,38 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
     load_stage(stg[s], s);
     __builtin_amdgcn_sched_barrier(0);
   }
+
+  if constexpr (FUSED) {
+    if (split == 0 && chunk == 0) {
+      constexpr int kPieces = C::kRowBytes / 16;
+      for (int i = tid; i < 2 * a.m * kPieces; i += kThreads) {
+        const int tensor = i / (a.m * kPieces);
+        const int j = (i / kPieces) % a.m;
+        const int c = i % kPieces;
+        const int64_t p = (int64_t)n + j;
+        if (p >= a.capacity) continue;
+        const char* src = (tensor ? vnew : knew) + (size_t)j * a.n_kv_heads * C::kRowBytes;
+        char* dst = const_cast<char*>(tensor ? vbase : kbase) + (size_t)p * C::kRowBytes;
+        reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(src)[c];
+        if (a.pos && h == 0 && tensor == 0 && c == 0) a.pos[(size_t)b * a.capacity + p] = (int32_t)p;
+      }
+    }
+    n = n <= 0x7fffffff - a.m ? n + a.m : 0x7fffffff;
+  } else {
+    n = max(a.seq_len[b], 0);
+  }
+  const RingMask rm = ring_mask(a, n);
+  n = min(n, a.limit);
+  const int last = n - 1;
+  const int tiles = (n + kTileKeys - 1) / kTileKeys;
+  const int my_tiles = split < tiles ? (tiles - split + n_splits - 1) / n_splits : 0;
+  const int my_stages = (my_tiles + C::kTps - 1) / C::kTps;
+  int last_visible[C::kRbw];
+#pragma unroll
+  for (int j = 0; j < C::kRbw; ++j)
+    last_visible[j] = (a.mode == kModeVerify) ? (n - a.m + row_j[j]) : (n - 1);
+  // the last key every row of the workgroup may attend (candidate 0 sees the fewest)
+  const int vis_all = min(last, (a.mode == kModeVerify) ? (n - a.m) : (n - 1));
 
   const float scale_log2 = a.sm_scale * kLog2e;
   float m_ref[C::kRbw];   // reference max (log2 units), shared by the row's four lanes
@@ -997,6 +1023,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, in
   __shared__ float red_m[256];
   __shared__ float4 red_o[256];
   __shared__ float red_l[256];
+  request_args(a);
 
   const int row_id = blockIdx.x;  // ((b * m + j) * Hq + hq)
   const int dim0 = blockIdx.y * (4 * kCols);

@@ -377,11 +377,12 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x;
   const int bhc = blockIdx.y;
-  const int chunk = bhc % n_chunks;
-  const int bh = bhc / n_chunks;
-  const int h = bh % a.n_kv_heads;
-  const int b = bh / a.n_kv_heads;
-  const int G = a.n_q_heads / a.n_kv_heads;
+  // (unsigned divisions: every operand is nonnegative, and their sequences are shorter)
+  const int chunk = (unsigned)bhc % (unsigned)n_chunks;
+  const int bh = (unsigned)bhc / (unsigned)n_chunks;
+  const int h = (unsigned)bh % (unsigned)a.n_kv_heads;
+  const int b = (unsigned)bh / (unsigned)a.n_kv_heads;
+  const int G = (unsigned)a.n_q_heads / (unsigned)a.n_kv_heads;
   const int rows = G * a.m;
   const int row0 = chunk * chunk_rows;
   const int row_end = min(rows, row0 + chunk_rows);
@@ -410,8 +411,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
     row_ok[rb] = row < row_end;
     // padding rows load the last real row (never written out; no select, so no early wait)
     const int row_q = row_ok[rb] ? row : row_end - 1;
-    const int jq = row_q / G;
-    const int hq = h * G + row_q % G;
+    const int jq = (unsigned)row_q / (unsigned)G;
+    const int hq = h * G + (unsigned)row_q % (unsigned)G;
     row_j[rb] = jq;
     if (QOp::kInLds && rb != wave) continue;  // LDS copy: one wave per row block
     const size_t qoff = ((size_t)(b * a.m + jq) * a.n_q_heads + hq) * D;
@@ -676,11 +677,12 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   const int d0 = (wave % C::kSplitD) * C::kDw;
   const int split = blockIdx.x;
   const int bhc = blockIdx.y;
-  const int chunk = bhc % n_chunks;
-  const int bh = bhc / n_chunks;
-  const int h = bh % a.n_kv_heads;
-  const int b = bh / a.n_kv_heads;
-  const int G = a.n_q_heads / a.n_kv_heads;
+  // (unsigned divisions: every operand is nonnegative, and their sequences are shorter)
+  const int chunk = (unsigned)bhc % (unsigned)n_chunks;
+  const int bh = (unsigned)bhc / (unsigned)n_chunks;
+  const int h = (unsigned)bh % (unsigned)a.n_kv_heads;
+  const int b = (unsigned)bh / (unsigned)a.n_kv_heads;
+  const int G = (unsigned)a.n_q_heads / (unsigned)a.n_kv_heads;
   const int rows = G * a.m;
   const int row_end = min(rows, chunk * chunk_rows + chunk_rows);
   const int r16 = lane & 15;
@@ -703,8 +705,8 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
     const int row = chunk * chunk_rows + (rb0 + kWavesPerBlock * j) * 16 + r16;
     row_ok[j] = row < row_end;
     const int row_q = row_ok[j] ? row : row_end - 1;
-    const int jq = row_q / G;
-    const int hq = h * G + row_q % G;
+    const int jq = (unsigned)row_q / (unsigned)G;
+    const int hq = h * G + (unsigned)row_q % (unsigned)G;
     row_j[j] = jq;
     const size_t qoff = ((size_t)(b * a.m + jq) * a.n_q_heads + hq) * D;
 #pragma unroll
@@ -1025,18 +1027,21 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, in
   __shared__ float red_l[256];
   request_args(a);
 
-  const int row_id = blockIdx.x;  // ((b * m + j) * Hq + hq)
+  // index arithmetic in unsigned ints (all values are nonnegative; the unsigned divisions are
+  // shorter instruction sequences than the signed ones)
+  const unsigned row_id = blockIdx.x;  // ((b * m + j) * Hq + hq)
   const int dim0 = blockIdx.y * (4 * kCols);
-  const int hq = row_id % a.n_q_heads;
-  const int bj = row_id / a.n_q_heads;
-  const int j = bj % a.m;
-  const int b = bj / a.m;
-  const int G = a.n_q_heads / a.n_kv_heads;
-  const int h = hq / G;
-  const int row = j * G + (hq % G);
-  const int chunk = row / chunk_rows;
-  const int rloc = row % chunk_rows;
-  const size_t base = ((size_t)(b * a.n_kv_heads + h) * n_chunks + chunk) * n_splits;
+  const unsigned nq = a.n_q_heads, nkv = a.n_kv_heads, um = a.m, crows = chunk_rows;
+  const unsigned hq = row_id % nq;
+  const unsigned bj = row_id / nq;
+  const unsigned j = bj % um;
+  const unsigned b = bj / um;
+  const unsigned G = nq / nkv;
+  const unsigned h = hq / G;
+  const unsigned row = j * G + (hq % G);
+  const unsigned chunk = row / crows;
+  const int rloc = row % crows;
+  const size_t base = ((size_t)(b * nkv + h) * n_chunks + chunk) * n_splits;
   const int rows16 = 16 * nr;
   const int tid = threadIdx.x;
   const int col = tid % kCols;

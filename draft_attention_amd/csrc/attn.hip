@@ -19,8 +19,8 @@
 // transposed in registers with v_perm_b32 into the V^T operand. 16-key tiles are dealt grid-stride
 // over all wavefronts of the launch (all workgroups sweep the cache together), and each wavefront
 // keeps the next tile's loads in flight while it computes the current one. At the end the
-// wavefronts combine their states through LDS and wavefront 0 writes one partial (o unnormalised,
-// running max in log2 units, running sum) per query row.
+// wavefronts combine their states through LDS, each wavefront a quarter of the dims, into one
+// partial (o unnormalised, running max in log2 units, running sum) per query row.
 //
 // Kernel 1b (attn_coop_kernel, more rows: verification): the four wavefronts of a workgroup share
 // each tile through an LDS stage (see the comment above the kernel).

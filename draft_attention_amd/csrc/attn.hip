@@ -147,11 +147,7 @@ template <int D, int NR, bool BF16>
 struct QOperand {
   using F = Frag<D, BF16>;
   typedef typename std::conditional<BF16, bf16x8_t, f32x4_t>::type Vec;
-#ifdef WMTP_WIDE_QREG
-  static constexpr bool kInLds = false;
-#else
   static constexpr bool kInLds = NR * F::kQRegs * 4 >= 64;
-#endif
   Vec reg[kInLds ? 1 : NR][kInLds ? 1 : F::kQRegs];
   const uint4* lds;
   int lane;
@@ -355,9 +351,6 @@ constexpr bool pipelined() {
   constexpr int q = QOperand<D, NR, BF16>::kInLds ? 0 : NR * F::kQRegs * 4;
   constexpr int o = NR * F::kBlocks * 4;
   constexpr int tile = F::kQRegs * 4 + 4 * F::kSets * F::kVWords;
-#ifdef WMTP_WIDE
-  if (NR == 4 && D == 128 && BF16) return true;
-#endif
   return q + o + 2 * tile <= 224 && o <= 96;
 }
 

@@ -27,6 +27,12 @@ struct SplitPlan {
 
 constexpr int kTileKeys = 16;       // keys per MFMA tile
 constexpr int kWavesPerBlock = 4;   // wavefronts per workgroup (interleaved tiles of one range)
+// Build-time tuning knobs (hipcc -D...), each defaulting to the value measured best on MI355X:
+//   WMTP_TARGET_BLOCKS_SPLIT / _COOP  workgroups per call of each attention kernel (below)
+//   WMTP_ALLOW_COOP                   0: every row count on the key-split kernel
+//   WMTP_COOP_TPS, WMTP_COOP_PREFETCH tiles per LDS stage, stages in flight (cooperative kernel)
+//   WMTP_COOP_WPC                     workgroups per CU the cooperative kernel is compiled for
+//   WMTP_MIN_TILES_PER_WAVE           smallest share of a wavefront when the planner splits keys
 // workgroups per call (256 CUs), measured best for each kernel on MI355X at L = 1M
 #ifndef WMTP_TARGET_BLOCKS_SPLIT
 #define WMTP_TARGET_BLOCKS_SPLIT 256

@@ -8,12 +8,13 @@ import math
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from draft_attention_amd import binding as W
 from draft_attention_amd import synth
 from gpu_common import (DEV, append_all, append_each, compare, logical_kv, ocode, oracle_kv,
-                        run_full, run_verify, run_windowed, say, tdtype)
+                        run_full, run_verify, run_windowed, say, tdtype, tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -76,3 +77,47 @@ def test_random_shape(seed):
             out, lse = run_verify(cache, q, Hq, scale, bound)
             ref_o, ref_l = oracle.verify(synth.host_array(q), ocode(dt), kv, lens, scale)
     compare(out, lse, ref_o, ref_l, dt, f"random {c['kind']} case {seed}")
+
+
+N_STEP_CASES = 18
+
+
+@pytest.mark.parametrize("seed", range(N_STEP_CASES))
+def test_random_fused_step(seed):
+    """The fused calls (append, then attend, in one call) on random shapes: the result covers the
+    appended tokens, and the cache holds them afterwards (its length grew by their count)."""
+    c = _case(100 + seed)
+    dt, d, Hkv, G, B, lens = c["dt"], c["d"], c["Hkv"], c["G"], c["B"], c["lens"]
+    Hq = G * Hkv
+    scale = 1.0 / math.sqrt(d)
+    m = c.get("m", 1)
+    say(f"random fused step {seed}: {c}")
+    K, V = logical_kv(700 + seed, B, Hkv, d, max(lens), tdtype(dt))
+    kv = oracle_kv(K, V, dt)
+    pre = [n - m for n in lens]  # the step appends the last m positions of every sequence
+    kn = torch.stack([tokens(K, b, pre[b], lens[b]) for b in range(B)])
+    vn = torch.stack([tokens(V, b, pre[b], lens[b]) for b in range(B)])
+    q = synth.queries(750 + seed, 0, B, m, Hq, d, tdtype(dt), DEV)
+    out = torch.full((B, m, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    lse = torch.full((B, m, Hq), float("nan"), dtype=torch.float32, device=DEV)
+    if c["kind"] == "windowed":
+        cache = W.KVCache.ring(B, Hkv, d, c["S"], c["W"], tdtype(dt), slack=c["slack"])
+        append_each(cache, K, V, [0] * B, pre)
+        ws = W.workspace(B, Hq, Hkv, d, 1, cache.capacity)
+        W.wmtp_draft_step_windowed(cache, kn, vn, q, Hq, scale, out, lse, ws)
+        ref_o, ref_l = oracle.draft_windowed(synth.host_array(q), ocode(dt), kv, lens, c["S"],
+                                             c["W"], scale)
+    else:
+        cap = max(lens) + c["extra"] + 1
+        bound = max(lens) + (c["extra"] // 2)
+        cache = W.KVCache.contiguous(B, Hkv, d, cap, tdtype(dt))
+        append_each(cache, K, V, [0] * B, pre)
+        ws = W.workspace(B, Hq, Hkv, d, m, bound)
+        if c["kind"] == "full":
+            W.wmtp_draft_step_full(cache, kn, vn, q, Hq, scale, bound, out, lse, ws)
+            ref_o, ref_l = oracle.draft_full(synth.host_array(q), ocode(dt), kv, lens, scale)
+        else:
+            W.wmtp_verify_step(cache, kn, vn, q, m, Hq, scale, bound, out, lse, ws)
+            ref_o, ref_l = oracle.verify(synth.host_array(q), ocode(dt), kv, lens, scale)
+    compare(out, lse, ref_o, ref_l, dt, f"random fused {c['kind']} step {seed}")
+    assert cache.seq_len.cpu().tolist() == lens

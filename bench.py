@@ -413,6 +413,7 @@ def composite(W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log, iters: in
         lg = logits[:, :k + 1].contiguous()
         dr = drafts[:, :k].contiguous()
         ch = choice[:, :k + 1].contiguous()
+        qk = q4[:, :k + 1].contiguous()  # made once here, not a copy inside the timed iteration
 
         def run():
             cache = ring if form == "windowed" else full
@@ -423,9 +424,8 @@ def composite(W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log, iters: in
                 else:
                     W.wmtp_draft_step_full(full, tok_k[i:i + 1][None], tok_v[i:i + 1][None], q3,
                                            Hq, scale3, cap, out3, lse3, ws_full)
-            W.wmtp_verify_step(tgt, cand_k[:k + 1][None], cand_v[:k + 1][None],
-                               q4[:, :k + 1].contiguous(), k + 1, Hq4, scale4, cap4,
-                               out4[:, :k + 1], lse4[:, :k + 1], ws_ver)
+            W.wmtp_verify_step(tgt, cand_k[:k + 1][None], cand_v[:k + 1][None], qk, k + 1, Hq4,
+                               scale4, cap4, out4[:, :k + 1], lse4[:, :k + 1], ws_ver)
             W.wmtp_greedy_accept(lg, k, dr, ch, n_acc, nxt, n_drop, ws_acc)
             W.wmtp_ring_rollback(cache, n_drop)
             W.wmtp_ring_rollback(tgt, n_drop)
@@ -459,10 +459,11 @@ def composite(W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log, iters: in
     one_v = cand_v[:1][None]
     one = torch.ones((1,), dtype=torch.int32, device=dev)
     ws1 = W.workspace(1, Hq4, Hkv4, d4, 1, cap4, dev)
+    q1 = q4[:, :1].contiguous()
 
     def nospec():
-        W.wmtp_verify_step(tgt, one_k, one_v, q4[:, :1].contiguous(), 1, Hq4, scale4, cap4,
-                           out4[:, :1], lse4[:, :1], ws1)
+        W.wmtp_verify_step(tgt, one_k, one_v, q1, 1, Hq4, scale4, cap4, out4[:, :1], lse4[:, :1],
+                           ws1)
         W.wmtp_ring_rollback(tgt, one)  # keep the cache length fixed across repetitions
     res["no_speculation_step_us"] = round(timed(nospec), 1)
     res["note"] = ("attention-side cost of one decode iteration (eager launches); tokens per "

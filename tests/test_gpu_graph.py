@@ -199,3 +199,66 @@ def test_graph_replay_of_a_speculative_iteration():
         assert graphed.acc.tolist() == [1, 0]
         assert graphed.ring.seq_len.tolist() == [L + r + 1, L]
         assert graphed.tgt.seq_len.tolist() == [L + 2 * (r + 1), L + r + 1]
+
+
+def test_graph_replay_of_fused_verification_and_masw():
+    """The fused verification step on the cooperative kernel (its candidates stored by one
+    workgroup, the length advanced by the merge) and the MASW-style step (two reads, one merge),
+    captured together: replays equal the eager calls bit for bit, replay after replay."""
+    dt = torch.bfloat16
+    B, Hq, Hkv, d, m, S, Wn, n_slots = 2, 32, 2, 128, 4, 4, 64, 40
+    L, replays = 1500, 3
+    cap = L + (replays + 2) * m + 16
+    say(f"graph replay of the fused verification and the MASW step B={B} Hq={Hq} m={m}")
+    K, Vv = logical_kv(2301, B, Hkv, d, L, dt)
+    SK, SV = logical_kv(2302, B, Hkv, d, n_slots, dt)
+    cand_k = torch.stack([synth.token_rows(2303, synth.KNEW_ID, b, 0, m, Hkv, d, dt, DEV)
+                          for b in range(B)])
+    cand_v = torch.stack([synth.token_rows(2303, synth.VNEW_ID, b, 0, m, Hkv, d, dt, DEV)
+                          for b in range(B)])
+    qv = synth.queries(2304, 0, B, m, Hq, d, dt, DEV)
+    qd = synth.queries(2305, 0, B, 1, Hq // 2, d, dt, DEV)
+
+    class It:
+        def __init__(self):
+            self.tgt = W.KVCache.contiguous(B, Hkv, d, cap, dt)
+            append_all(self.tgt, K, Vv, [0] * B, L)
+            self.ring = W.KVCache.ring(B, Hkv, d, S, Wn, dt)
+            append_all(self.ring, K, Vv, [0] * B, L)
+            self.slots = W.KVCache.contiguous(B, Hkv, d, n_slots + 8, dt)
+            append_all(self.slots, SK, SV, [0] * B, n_slots)
+            self.ov = torch.zeros((B, m, Hq, d), dtype=torch.float32, device=DEV)
+            self.lv = torch.zeros((B, m, Hq), dtype=torch.float32, device=DEV)
+            self.om = torch.zeros((B, 1, Hq // 2, d), dtype=torch.float32, device=DEV)
+            self.lm = torch.zeros((B, 1, Hq // 2), dtype=torch.float32, device=DEV)
+            self.ws_v = W.workspace(B, Hq, Hkv, d, m, cap)
+            self.ws_m = W.masw_workspace(B, Hq // 2, Hkv, d, self.ring.capacity, n_slots + 8)
+
+        def run(self):
+            W.wmtp_verify_step(self.tgt, cand_k, cand_v, qv, m, Hq, 0.09, cap, self.ov, self.lv,
+                               self.ws_v)
+            W.wmtp_draft_attn_masw(self.ring, self.slots, qd, Hq // 2, 0.09, n_slots + 8, self.om,
+                                   self.lm, self.ws_m)
+
+        def state(self):
+            out = []
+            for c in (self.tgt, self.ring, self.slots):
+                out += [c.k.clone(), c.v.clone(), c.seq_len.clone()]
+            return out + [t.clone() for t in (self.ov, self.lv, self.om, self.lm)]
+
+    eager, graphed = It(), It()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graphed.run()
+    torch.cuda.synchronize()
+    side = It()
+    for r in range(replays):
+        say(f"  replay {r}")
+        eager.run()
+        g.replay()
+        side.run()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(eager.state(), graphed.state())):
+            assert torch.equal(a, b), f"replay {r}: tensor {i} differs from the eager run"
+        assert graphed.tgt.seq_len.tolist() == [L + (r + 1) * m] * B

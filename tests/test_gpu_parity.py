@@ -267,3 +267,31 @@ def test_empty_sequences_give_zero_and_minus_inf():
     ref_o, ref_l = oracle.verify(synth.host_array(qv[1:]), ocode(dt), oracle_kv(K[1:], V[1:], dt),
                                  [2], 0.1)
     compare(out[1:], lse[1:], ref_o, ref_l, dt, "verify with n < m")
+
+
+def test_null_lse_gives_the_same_outputs():
+    """lse is optional: with a NULL lse every read writes the same outputs, bit for bit."""
+    dt, d, Hkv, B = "bf16", 128, 2, 2
+    say("null lse: windowed, full and verify (split and cooperative kernels)")
+    K, V = logical_kv(47, B, Hkv, d, 3000, tdtype(dt))
+    ring = W.KVCache.ring(B, Hkv, d, 4, 256, tdtype(dt))
+    append_each(ring, K, V, [0] * B, [3000, 700])
+    cache = W.KVCache.contiguous(B, Hkv, d, 3008, tdtype(dt))
+    append_each(cache, K, V, [0] * B, [3000, 700])
+    for Hq, m in ((16, 1), (16, 4)):  # 8 rows (key-split) and 32 rows (cooperative) per KV head
+        q = synth.queries(48, 0, B, m, Hq, d, tdtype(dt), DEV)
+        calls = [("verify", lambda o, l: W.wmtp_verify_attn(
+            cache, q, m, Hq, 0.1, 3000, o, l, W.workspace(B, Hq, Hkv, d, m, 3000)))]
+        if m == 1:
+            calls += [
+                ("windowed", lambda o, l: W.wmtp_draft_attn_windowed(
+                    ring, q, Hq, 0.1, o, l, W.workspace(B, Hq, Hkv, d, 1, ring.capacity))),
+                ("full", lambda o, l: W.wmtp_draft_attn_full(
+                    cache, q, Hq, 0.1, 3000, o, l, W.workspace(B, Hq, Hkv, d, 1, 3000)))]
+        for name, call in calls:
+            o1 = torch.full((B, m, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+            l1 = torch.empty((B, m, Hq), dtype=torch.float32, device=DEV)
+            o2 = torch.full_like(o1, float("nan"))
+            call(o1, l1)
+            call(o2, None)
+            assert torch.equal(o1, o2), f"{name} (m={m}): outputs differ without lse"

@@ -4,6 +4,10 @@ Every output the oracle can afford is compared (all heads of every draft step at
 few seconds of float64 on the host); the batched 10,000-step ring run is compared at sampled steps
 (first, last, every 2,000th, and each sequence's first window wrap), with the ring's bytes and
 position tags checked bit for bit at the same steps.
+
+The benchmark times the one-call steps (wmtp_draft_step_windowed / _full, wmtp_verify_step). At the
+million-token sizes they run beside the separate calls on the same bytes and must equal them bit for
+bit (outputs, lse, cache rows, tags, lengths), so the oracle comparison covers them too.
 """
 import math
 
@@ -15,7 +19,7 @@ import oracle
 from draft_attention_amd import binding as W
 from draft_attention_amd import configs, synth
 from gpu_common import (DEV, TOL, append_all, append_each, compare, ocode, oracle_kv, run_full,
-                        run_verify, run_windowed, say, tdtype)
+                        run_verify, run_windowed, say, tdtype, tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,9 +41,11 @@ def kv_of(cache: W.KVCache, n: int, dtname: str) -> oracle.LogicalKV:
     return oracle_kv(cache.k[:, :, :n], cache.v[:, :, :n], dtname)
 
 
-def draft_steps(wl, k_scale=None, full_heads=None):
+def draft_steps(wl, k_scale=None, full_heads=None, fused=False):
     """The draft loop of one workload: k steps, each appending its token to the ring and to the
-    contiguous cache, then attending (windowed and full) with that step's query."""
+    contiguous cache, then attending (windowed and full) with that step's query. With `fused`, the
+    one-call steps run beside them on a copy of the ring and on the same contiguous rows (own
+    length counter) and must give the same bits."""
     dt = tdtype(wl.dtype)
     L, k, d = wl.context, wl.draft_depth, wl.head_dim
     scale = 1.0 / math.sqrt(d)
@@ -53,6 +59,15 @@ def draft_steps(wl, k_scale=None, full_heads=None):
     append_each(ring, cache.k, cache.v, [0], [L])
     model = oracle.RingModel(1, wl.sink, wl.window)
     model.append(0, L)
+    if fused:
+        ring2 = W.KVCache(ring.k.clone(), ring.v.clone(), ring.pos.clone(), ring.seq_len.clone(),
+                          1, ring.n_kv_heads, d, ring.capacity, ring.sink, ring.window, ring.dtype)
+        view2 = W.KVCache(cache.k, cache.v, None, cache.seq_len.clone(), 1, cache.n_kv_heads, d,
+                          cache.capacity, cache.capacity, 0, cache.dtype)
+        ws_win = W.workspace(1, wl.n_q_heads, ring.n_kv_heads, d, 1, ring.capacity)
+        ws_full = W.workspace(1, wl.n_q_heads, cache.n_kv_heads, d, 1, L + k)
+        out2 = torch.empty((1, 1, wl.n_q_heads, d), dtype=torch.float32, device=DEV)
+        lse2 = torch.empty((1, 1, wl.n_q_heads), dtype=torch.float32, device=DEV)
     worst = 0.0
     for i in range(k):
         n = L + i + 1
@@ -71,6 +86,20 @@ def draft_steps(wl, k_scale=None, full_heads=None):
                                     _head_subset(kv, heads, wl), [n], scale)
         worst = max(worst, compare(of[:, :, heads], lf[:, :, heads], rf, rlf, wl.dtype,
                                    f"full step {i} ({len(heads)} heads)")[0])
+        if fused:
+            kn = tokens(cache.k, 0, n - 1, n)[None]
+            vn = tokens(cache.v, 0, n - 1, n)[None]
+            W.wmtp_draft_step_windowed(ring2, kn, vn, q, wl.n_q_heads, scale, out2, lse2, ws_win)
+            assert torch.equal(out2, ow) and torch.equal(lse2, lw), f"fused windowed step {i}"
+            W.wmtp_draft_step_full(view2, kn, vn, q, wl.n_q_heads, scale, L + k, out2, lse2,
+                                   ws_full)
+            assert torch.equal(out2, of) and torch.equal(lse2, lf), f"fused full step {i}"
+            assert torch.equal(view2.seq_len, cache.seq_len), f"fused full step {i}: length"
+            say(f"  fused steps {i}: equal to append-then-attend bit for bit")
+    if fused:
+        for a, b_ in ((ring2.k, ring.k), (ring2.v, ring.v), (ring2.pos, ring.pos),
+                      (ring2.seq_len, ring.seq_len)):
+            assert torch.equal(a, b_), "fused windowed steps: ring state differs"
     # the ring holds exactly the sinks and the last W positions, bit for bit
     tags = ring.pos.cpu().numpy().astype(np.int64)
     assert np.array_equal(tags, model.tags)
@@ -123,12 +152,12 @@ def test_tiny_window_covers_all_equivalence():
 
 def test_mid_context_three_steps():
     wl = configs.MID
-    draft_steps(wl, k_scale=wl.k_scale)
+    draft_steps(wl, k_scale=wl.k_scale, fused=True)
 
 
 def test_million_token_five_steps():
     wl = configs.MILLION
-    draft_steps(wl)
+    draft_steps(wl, fused=True)
 
 
 def test_verify_million_tokens():
@@ -141,9 +170,20 @@ def test_verify_million_tokens():
     fill_prefix(cache, wl.seed, L + m, dt)
     kv = kv_of(cache, L + m, wl.dtype)  # the generator's bytes, before any kernel touches them
     cache.seq_len.fill_(L)
+    view2 = W.KVCache(cache.k, cache.v, None, cache.seq_len.clone(), 1, cache.n_kv_heads, d,
+                      cache.capacity, cache.capacity, 0, cache.dtype)
     append_all(cache, cache.k, cache.v, [L], m)  # the candidates, through the append path
     q = synth.queries(wl.seed, 0, 1, m, wl.n_q_heads, d, dt, DEV)
     out, lse = run_verify(cache, q, wl.n_q_heads, scale, L + m)
+    # the one-call verification step the benchmark times (append of the m candidates fused in),
+    # on the same rows with its own length counter: the same bits
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    ws = W.workspace(1, wl.n_q_heads, wl.n_kv_heads, d, m, L + m)
+    W.wmtp_verify_step(view2, tokens(cache.k, 0, L, L + m)[None], tokens(cache.v, 0, L, L + m)[None],
+                       q, m, wl.n_q_heads, scale, L + m, out2, lse2, ws)
+    assert torch.equal(out2, out) and torch.equal(lse2, lse), "fused verification step"
+    assert torch.equal(view2.seq_len, cache.seq_len), "fused verification step: length"
     ref, rl = oracle.verify(synth.host_array(q), ocode(wl.dtype), kv, [L + m], scale)
     compare(out, lse, ref, rl, wl.dtype, "verify at 1M")
     # the causal rows differ from one another only through the candidates they see

@@ -343,6 +343,23 @@ __device__ __forceinline__ int out_dim(int sx, int grp, int j) {
   return sx * F::kSetDims + F::kDpl * (4 * grp + j);
 }
 
+// Zeroes the V rows of the tile's keys past `last`. Their weights are 0, but 0 * NaN is NaN: the
+// first tile of a wavefront is requested against the host-side bound before seq_len is known, so
+// its keys past the length hold whatever those rows hold. Called on a wavefront-uniform branch,
+// only for a tile that reaches past `last`.
+template <int D, bool BF16>
+__device__ __forceinline__ void clear_past(Tile<D, BF16>& T, int t0, int last, int grp) {
+  using F = Frag<D, BF16>;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool keep = t0 + 4 * grp + j <= last;
+#pragma unroll
+    for (int sx = 0; sx < F::kSets; ++sx)
+#pragma unroll
+      for (int w = 0; w < F::kVWords; ++w) T.v[j][sx][w] = keep ? T.v[j][sx][w] : 0u;
+  }
+}
+
 // Whether a wavefront can hold two tiles (the next one in flight) beside its query operand and
 // accumulators without spilling: a register estimate in 32-bit registers per lane.
 template <int D, int NR, bool BF16>
@@ -507,24 +524,29 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
     // the computation it overlaps.
     if (t < n && t + kStride >= n) {
       // a single tile (the windowed read's usual share): nothing to overlap
+      if (t + kTileKeys - 1 > last) clear_past<D, BF16>(A, t, last, grp);
       compute_tile<D, NR, BF16, RING>(A, qf, t, last, last_visible, rm, grp, scale_log2, st);
       t = n;
     }
     while (t < n) {
       load_tile<D, BF16>(kbase, vbase, t + kStride, last, r16, grp, B, fresh, knew, vnew);
       __builtin_amdgcn_sched_barrier(0);
+      if (t + kTileKeys - 1 > last) clear_past<D, BF16>(A, t, last, grp);
       compute_tile<D, NR, BF16, RING>(A, qf, t, last, last_visible, rm, grp, scale_log2, st);
       load_tile<D, BF16>(kbase, vbase, t + 2 * kStride, last, r16, grp, A, fresh, knew, vnew);
       __builtin_amdgcn_sched_barrier(0);
-      if (t + kStride < n)
+      if (t + kStride < n) {
+        if (t + kStride + kTileKeys - 1 > last) clear_past<D, BF16>(B, t + kStride, last, grp);
         compute_tile<D, NR, BF16, RING>(B, qf, t + kStride, last, last_visible, rm, grp, scale_log2,
                                         st);
+      }
       t += 2 * kStride;
     }
   } else {
     // one register tile: loads of tile t + stride start once tile t is consumed
     (void)B;
     while (t < n) {
+      if (t + kTileKeys - 1 > last) clear_past<D, BF16>(A, t, last, grp);
       compute_tile<D, NR, BF16, RING>(A, qf, t, last, last_visible, rm, grp, scale_log2, st);
       t += kStride;
       if (t < n) load_tile<D, BF16>(kbase, vbase, t, last, r16, grp, A, fresh, knew, vnew);
@@ -757,7 +779,14 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
       dst[l] = stream_load16(row + c * 16);
     }
   };
-  auto store_stage = [&](const uint4(&src)[C::kLoads], int buf) {
+  // Staged tiles may run past the length (the first stages are requested against the host-side
+  // bound, and a workgroup's rounds end in tiles past its share). Their keys get weight 0, but
+  // 0 * NaN is NaN, so a stage that reaches past `clip_last` (the last attended key, set once
+  // seq_len is known) stores zeros for those keys instead (a workgroup-uniform branch, taken only
+  // by such stages).
+  int clip_last = 0x7fffffff;
+  auto store_stage = [&](const uint4(&src)[C::kLoads], int buf, int stage) {
+    const bool clip = tile_start(stage * C::kTps + C::kTps - 1) + kTileKeys - 1 > clip_last;
 #pragma unroll
     for (int l = 0; l < C::kLoads; ++l) {
       const int q = tid + kThreads * l;
@@ -765,8 +794,10 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
       const int tensor = (q / (16 * C::kChunks)) & 1;
       const int key = (q / C::kChunks) % 16;
       const int c = q % C::kChunks;
+      uint4 x = src[l];
+      if (clip && tile_start(stage * C::kTps + u) + key > clip_last) x = make_uint4(0u, 0u, 0u, 0u);
       *reinterpret_cast<uint4*>(&sm_tile[buf][(2 * u + tensor) * C::kTileBytes +
-                                              coop_slot<D, NB, BF16>(key, c, tensor)]) = src[l];
+                                              coop_slot<D, NB, BF16>(key, c, tensor)]) = x;
     }
   };
 
@@ -804,6 +835,7 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   const RingMask rm = ring_mask(a, n);
   n = min(n, a.limit);
   const int last = n - 1;
+  clip_last = last;
   const int tiles = (n + kTileKeys - 1) / kTileKeys;
   const int my_tiles = split < tiles ? (tiles - split + n_splits - 1) / n_splits : 0;
   const int my_stages = (my_tiles + C::kTps - 1) / C::kTps;
@@ -957,7 +989,7 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
     for (int s = 0; s < C::kPrefetch; ++s) {
       const int st = base + s;
       const int buf = st & 1;
-      store_stage(stg[s], buf);
+      store_stage(stg[s], buf, st);
       load_stage(stg[s], st + C::kPrefetch);
       __syncthreads();  // stage st visible; every wavefront is done with stage st-1's buffer
 #pragma unroll

@@ -295,3 +295,73 @@ def test_null_lse_gives_the_same_outputs():
             call(o1, l1)
             call(o2, None)
             assert torch.equal(o1, o2), f"{name} (m={m}): outputs differ without lse"
+
+
+# ------------------------------------------------------------------------------------------
+# rows past a sequence's length are never attended: whatever bytes they hold (NaN here), the
+# results do not change. Short sequences under a larger host bound make the first tiles straddle
+# the end (key-split kernel) and the staged tiles run past it (cooperative kernel).
+# ------------------------------------------------------------------------------------------
+def _poison(cache: W.KVCache, lens, from_offset: int = 0):
+    """Copy of `cache` whose rows (ring: slots) at or past each length hold NaN bytes."""
+    c = W.KVCache(cache.k.clone(), cache.v.clone(),
+                  None if cache.pos is None else cache.pos.clone(), cache.seq_len.clone(),
+                  cache.batch, cache.n_kv_heads, cache.head_dim, cache.capacity, cache.sink,
+                  cache.window, cache.dtype)
+    for b, n in enumerate(lens):
+        r0 = n + from_offset
+        if r0 < cache.capacity:
+            c.k[b, :, r0:] = float("nan")
+            c.v[b, :, r0:] = float("nan")
+    return c
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("bf16", 256), ("f32", 64), ("f32", 128)])
+def test_bytes_past_the_length_do_not_reach_results(dt, d):
+    Hkv, S, Wn, lens, bound = 2, 4, 256, [20, 37, 300], 512
+    B = len(lens)
+    say(f"NaN rows past the length: {dt} d={d} lens={lens} bound={bound}")
+    K, V = logical_kv(81, B, Hkv, d, max(lens) + 8, tdtype(dt))
+    cache = W.KVCache.contiguous(B, Hkv, d, bound + 8, tdtype(dt))
+    append_each(cache, K, V, [0] * B, lens)
+    ring = W.KVCache.ring(B, Hkv, d, S, Wn, tdtype(dt))
+    append_each(ring, K, V, [0] * B, lens)
+    kn = torch.stack([K[b, :, lens[b]:lens[b] + 4].permute(1, 0, 2) for b in range(B)]).contiguous()
+    vn = torch.stack([V[b, :, lens[b]:lens[b] + 4].permute(1, 0, 2) for b in range(B)]).contiguous()
+    k1, v1 = kn[:, :1].contiguous(), vn[:, :1].contiguous()  # a draft step's token
+
+    def attn(c, q, Hq, m, kind):
+        o = torch.full((B, m, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+        l = torch.full((B, m, Hq), float("nan"), dtype=torch.float32, device=DEV)
+        if kind == "windowed":
+            W.wmtp_draft_attn_windowed(c, q, Hq, 0.1, o, l, W.workspace(B, Hq, Hkv, d, 1, c.capacity))
+        elif kind == "full":
+            W.wmtp_draft_attn_full(c, q, Hq, 0.1, bound, o, l, W.workspace(B, Hq, Hkv, d, 1, bound))
+        elif kind == "verify":
+            W.wmtp_verify_attn(c, q, m, Hq, 0.1, bound, o, l, W.workspace(B, Hq, Hkv, d, m, bound))
+        elif kind == "step_windowed":
+            W.wmtp_draft_step_windowed(c, k1, v1, q, Hq, 0.1, o, l,
+                                       W.workspace(B, Hq, Hkv, d, 1, c.capacity))
+        elif kind == "step_full":
+            W.wmtp_draft_step_full(c, k1, v1, q, Hq, 0.1, bound, o, l,
+                                   W.workspace(B, Hq, Hkv, d, 1, bound))
+        else:  # verify_step
+            W.wmtp_verify_step(c, kn[:, :m].contiguous(), vn[:, :m].contiguous(), q, m, Hq, 0.1,
+                               bound, o, l, W.workspace(B, Hq, Hkv, d, m, bound))
+        return o, l
+
+    # G = 4 (key-split kernel) and G = 16 with m = 4 (64 rows: cooperative kernel where it runs)
+    cases = [(8, 1, "windowed", ring), (8, 1, "full", cache), (8, 1, "step_windowed", ring),
+             (8, 1, "step_full", cache), (8, 4, "verify", cache), (32, 4, "verify", cache),
+             (32, 4, "verify_step", cache), (32, 1, "windowed", ring), (32, 1, "full", cache)]
+    for Hq, m, kind, base in cases:
+        q = synth.queries(82, m, B, m, Hq, d, tdtype(dt), DEV)
+        clean = W.KVCache(base.k.clone(), base.v.clone(),
+                          None if base.pos is None else base.pos.clone(), base.seq_len.clone(),
+                          B, Hkv, d, base.capacity, base.sink, base.window, base.dtype)
+        dirty = _poison(base, lens)
+        o1, l1 = attn(clean, q, Hq, m, kind)
+        o2, l2 = attn(dirty, q, Hq, m, kind)
+        assert torch.isfinite(o1).all(), f"{kind} Hq={Hq} m={m}: non-finite output"
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), \
+            f"{kind} Hq={Hq} m={m}: rows past the length changed the results"

@@ -54,7 +54,9 @@
  * wmtp_status WITHOUT launching anything or touching any buffer when they are invalid. A HIP launch
  * failure returns WMTP_ERR_HIP. No C++ exception or abort crosses this ABI. Device-side contents
  * (seq_len, the data) cannot be validated on the host; the kernels never access memory outside the
- * buffers described, whatever seq_len holds (see each call).
+ * buffers described, whatever seq_len holds (see each call). Rows (ring slots) at or past a
+ * sequence's length may hold any bytes, NaN and Inf included: the attention calls may read them
+ * but they never reach out or lse, so a cache need not be cleared when it is allocated.
  */
 #ifndef WMTP_H
 #define WMTP_H

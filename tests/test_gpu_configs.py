@@ -2,8 +2,8 @@
 
 Every output the oracle can afford is compared (all heads of every draft step at 1M context take a
 few seconds of float64 on the host); the batched 10,000-step ring run is compared at sampled steps
-(first, last, every 2,000th, and each sequence's first window wrap), with the ring's bytes and
-position tags checked bit for bit at the same steps.
+(first, last, every 500th, and every step at which a sequence's window wraps back onto its first
+window slot), with the ring's bytes and position tags checked bit for bit at the same steps.
 
 The benchmark times the one-call steps (wmtp_draft_step_windowed / _full, wmtp_verify_step). At the
 million-token sizes they run beside the separate calls on the same bytes and must equal them bit for
@@ -216,11 +216,17 @@ def test_batched_ring_10000_decode_steps():
     W.wmtp_ring_append(ring, tok(Ks, S, S + Wn), tok(Vs, S, S + Wn), Wn)
     kv = oracle.LogicalKV(synth.host_array(Ks), synth.host_array(Vs), ocode(wl.dtype),
                           [[(0, 0, S), (lens[b] - Wn, S, span)] for b in range(B)])
-    # sampled steps: first, last, every 2000th, and for each sequence the step whose token is the
-    # first to wrap onto window slot S
-    sample = {0, 1, steps - 1} | set(range(0, steps, 2000))
+    # sampled steps: first, last, every 500th, and for each sequence every step whose token wraps
+    # onto window slot S (its position p has (p - S) % W == 0)
+    sample = {0, 1, steps - 1} | set(range(0, steps, 500))
     for b in range(B):
-        sample.add((S - lens[b]) % Wn)
+        sample |= set(range((S - lens[b]) % Wn, steps, Wn))
+    say(f"{len(sample)} sampled steps")
+    # host ring model of every append so far, advanced to each sampled step
+    model = oracle.RingModel(B, S, Wn)
+    for b in range(B):
+        model.append(b, lens[b])
+    in_model = 0  # draft steps the model has appended
     ws = W.workspace(B, Hq, Hkv, d, 1, S + Wn)
     out = torch.empty((B, 1, Hq, d), dtype=torch.float32, device=DEV)
     lse = torch.empty((B, 1, Hq), dtype=torch.float32, device=DEV)
@@ -242,9 +248,10 @@ def test_batched_ring_10000_decode_steps():
             ref, rl = oracle.draft_windowed(synth.host_array(qs[i - c0]), ocode(wl.dtype), kv, n,
                                             S, Wn, scale)
             worst = max(worst, compare(out, lse, ref, rl, wl.dtype, f"batched step {i}")[0])
-            model = oracle.RingModel(B, S, Wn)  # every append up to now, simulated in bulk
             for b in range(B):
-                model.append(b, n[b])
+                model.append(b, i + 1 - in_model)
+            in_model = i + 1
+            assert np.array_equal(model.n, n)
             assert np.array_equal(ring.pos.cpu().numpy().astype(np.int64), model.tags), f"tags {i}"
             rk, rv = oracle.ring_expected(model, kv)
             hk, hv = synth.host_array(ring.k), synth.host_array(ring.v)

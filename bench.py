@@ -295,6 +295,8 @@ def main():
     b_app4 = 2 * 2 * m * Hkv4 * d4 * 2
     step_bytes = k * (b_win + b_full + 2 * b_app3) + b_ver + b_app4
     ms_step = total_ms / args.steps
+    win_cold = sweep_res["windowed_us_cold"][-1]["p50"] if sweep_res else None
+    full_cold = sweep_res["full_us_cold"][-1]["p50"] if sweep_res else None
     gbs = lambda nbytes, us: nbytes / (us * 1e-6) / 1e9
     result = {
         "metric": "draft-step attn µs & HBM GB/s at 1M ctx, windowed vs full (1 GPU)",
@@ -322,11 +324,18 @@ def main():
             "full_attn": round(mean_us["full_attn"], 2),
             "full_attn_plus_append": round(mean_us["full_step"], 2),
             "full_over_windowed": round(mean_us["full_step"] / mean_us["win_step"], 1),
+            "windowed_attn_cold_p50": win_cold,
+            "full_attn_cold_p50": full_cold,
+            "timing": "*_attn: the attention calls alone, back to back behind a backlog read "
+                      "(warm: the windowed ring was read by the previous call); "
+                      "*_plus_append: the one-call steps inside the timed decode iterations; "
+                      "*_cold_p50: median single call after a cache flush (sweep at L=1048576)",
         },
         "hbm_gbs": {
             "windowed_attn": round(gbs(b_win, mean_us["win_attn"]), 1),
             "full_attn": round(gbs(b_full, mean_us["full_attn"]), 1),
             "verify_attn": round(gbs(b_ver, mean_us["ver_attn"]), 1),
+            "windowed_attn_cold": None if win_cold is None else round(gbs(b_win, win_cold), 1),
         },
         "verify_us": {"attn": round(mean_us["ver_attn"], 2),
                       "attn_plus_append": round(mean_us["ver_step"], 2)},

@@ -108,12 +108,26 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+_current_stream = None
+
+
 def _stream(stream) -> Optional[int]:
+    """The hipStream_t to enqueue on: the given stream, else torch's current stream of the current
+    device (looked up through torch's raw-handle accessor when it has one: constructing a
+    torch.cuda.Stream object per call costs a few microseconds of host time)."""
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
-    import torch
+    global _current_stream
+    if _current_stream is None:
+        import torch
 
-    return torch.cuda.current_stream().cuda_stream
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        dev = getattr(torch._C, "_cuda_getDevice", None)
+        if raw is not None and dev is not None:
+            _current_stream = lambda: raw(dev())
+        else:
+            _current_stream = lambda: torch.cuda.current_stream().cuda_stream
+    return _current_stream()
 
 
 def _done(status: int, what: str, check: bool) -> int:
@@ -122,9 +136,13 @@ def _done(status: int, what: str, check: bool) -> int:
     return status
 
 
-@dataclass
+@dataclass(eq=False)
 class KVCache:
-    """Device tensors of one cache plus its geometry; ``desc()`` gives the C descriptor."""
+    """Device tensors of one cache plus its geometry; ``desc()`` gives the C descriptor.
+
+    The descriptor is validated and built on first use and kept until a field is reassigned, so
+    a cache tensor must not be resized or re-pointed in place (``resize_``, ``set_``) once the
+    cache has been used; assign a new tensor to the field instead."""
 
     k: object
     v: object
@@ -168,10 +186,27 @@ class KVCache:
         return cls.allocate(batch, n_kv_heads, head_dim, capacity, capacity, 0, torch_dtype,
                             device, with_pos)
 
+    def __setattr__(self, name, value):
+        object.__setattr__(self, name, value)
+        if name != "_c":
+            object.__setattr__(self, "_c", None)  # geometry or a tensor changed: rebuild
+
     def desc(self) -> wmtp_kv:
-        return wmtp_kv(_ptr(self.k), _ptr(self.v), _ptr(self.pos), _ptr(self.seq_len),
-                       self.batch, self.n_kv_heads, self.head_dim, self.capacity, self.sink,
-                       self.window, self.dtype)
+        c = self.__dict__.get("_c")
+        if c is None:
+            # the cache tensors must be device memory, dense, and as large as the geometry says
+            # (the kernels index them by it)
+            eb = 2 if self.dtype == WMTP_BF16 else 4
+            rows = self.batch * self.n_kv_heads * self.capacity * self.head_dim
+            _numel_ok(self.k, rows, eb, "cache.k")
+            _numel_ok(self.v, rows, eb, "cache.v")
+            _numel_ok(self.pos, self.batch * self.capacity, 4, "cache.pos")
+            _numel_ok(self.seq_len, self.batch, 4, "cache.seq_len")
+            c = wmtp_kv(_ptr(self.k), _ptr(self.v), _ptr(self.pos), _ptr(self.seq_len),
+                        self.batch, self.n_kv_heads, self.head_dim, self.capacity, self.sink,
+                        self.window, self.dtype)
+            object.__setattr__(self, "_c", c)
+        return c
 
 
 def dtype_code(torch_dtype) -> int:
@@ -199,8 +234,7 @@ def _numel_ok(t, count: int, elem_bytes: int, name: str) -> None:
         raise ValueError(f"wmtp: {name} holds {t.numel()} elements, the call needs {count}")
 
 
-def _check_attn(cache, q, m: int, n_q_heads: int, out, lse) -> None:
-    d = _desc(cache)
+def _check_attn(d: wmtp_kv, q, m: int, n_q_heads: int, out, lse) -> None:
     eb = 2 if d.dtype == WMTP_BF16 else 4
     rows = d.batch * m * n_q_heads
     _numel_ok(q, rows * d.head_dim, eb, "q")
@@ -208,26 +242,19 @@ def _check_attn(cache, q, m: int, n_q_heads: int, out, lse) -> None:
     _numel_ok(lse, rows, 4, "lse")
 
 
-def _check_append(cache, k_new, v_new, n_new: int) -> None:
-    d = _desc(cache)
+def _check_append(d: wmtp_kv, k_new, v_new, n_new: int) -> None:
     eb = 2 if d.dtype == WMTP_BF16 else 4
     count = d.batch * max(n_new, 0) * d.n_kv_heads * d.head_dim
     _numel_ok(k_new, count, eb, "k_new")
     _numel_ok(v_new, count, eb, "v_new")
-    if isinstance(cache, KVCache):
-        cnt = d.batch * d.n_kv_heads * d.capacity * d.head_dim
-        _numel_ok(cache.k, cnt, eb, "cache.k")
-        _numel_ok(cache.v, cnt, eb, "cache.v")
-        _numel_ok(cache.pos, d.batch * d.capacity, 4, "cache.pos")
-        _numel_ok(cache.seq_len, d.batch, 4, "cache.seq_len")
 
 
 # ------------------------------------------------------------------------------------------
 # the C ABI, one function each
 # ------------------------------------------------------------------------------------------
 def wmtp_ring_append(cache, k_new, v_new, n_new: int, stream=None, check=True) -> int:
-    _check_append(cache, k_new, v_new, n_new)
     d = _desc(cache)
+    _check_append(d, k_new, v_new, n_new)
     st = lib().wmtp_ring_append(ctypes.byref(d), _ptr(k_new), _ptr(v_new), int(n_new),
                                 _stream(stream))
     return _done(st, "wmtp_ring_append", check)
@@ -235,8 +262,8 @@ def wmtp_ring_append(cache, k_new, v_new, n_new: int, stream=None, check=True) -
 
 def wmtp_draft_attn_windowed(ring, q, n_q_heads: int, sm_scale: float, out, lse, ws,
                              ws_bytes: Optional[int] = None, stream=None, check=True) -> int:
-    _check_attn(ring, q, 1, n_q_heads, out, lse)
     d = _desc(ring)
+    _check_attn(d, q, 1, n_q_heads, out, lse)
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     st = lib().wmtp_draft_attn_windowed(ctypes.byref(d), _ptr(q), int(n_q_heads), float(sm_scale),
                                         _ptr(out), _ptr(lse), _ptr(ws), int(nbytes),
@@ -246,8 +273,8 @@ def wmtp_draft_attn_windowed(ring, q, n_q_heads: int, sm_scale: float, out, lse,
 
 def wmtp_draft_attn_full(cache, q, n_q_heads: int, sm_scale: float, max_seq_len: int, out, lse,
                          ws, ws_bytes: Optional[int] = None, stream=None, check=True) -> int:
-    _check_attn(cache, q, 1, n_q_heads, out, lse)
     d = _desc(cache)
+    _check_attn(d, q, 1, n_q_heads, out, lse)
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     st = lib().wmtp_draft_attn_full(ctypes.byref(d), _ptr(q), int(n_q_heads), float(sm_scale),
                                     int(max_seq_len), _ptr(out), _ptr(lse), _ptr(ws), int(nbytes),
@@ -257,8 +284,8 @@ def wmtp_draft_attn_full(cache, q, n_q_heads: int, sm_scale: float, max_seq_len:
 
 def wmtp_verify_attn(cache, q, m: int, n_q_heads: int, sm_scale: float, max_seq_len: int, out,
                      lse, ws, ws_bytes: Optional[int] = None, stream=None, check=True) -> int:
-    _check_attn(cache, q, m, n_q_heads, out, lse)
     d = _desc(cache)
+    _check_attn(d, q, m, n_q_heads, out, lse)
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     st = lib().wmtp_verify_attn(ctypes.byref(d), _ptr(q), int(m), int(n_q_heads),
                                 float(sm_scale), int(max_seq_len), _ptr(out), _ptr(lse),
@@ -289,9 +316,9 @@ def wmtp_llc_flush(buf, value: int = 0, stream=None, check=True) -> int:
 def wmtp_draft_step_windowed(ring, k_new, v_new, q, n_q_heads: int, sm_scale: float, out, lse, ws,
                              ws_bytes: Optional[int] = None, stream=None, check=True) -> int:
     """Append one token per sequence, then the windowed draft attention (one call)."""
-    _check_append(ring, k_new, v_new, 1)
-    _check_attn(ring, q, 1, n_q_heads, out, lse)
     d = _desc(ring)
+    _check_append(d, k_new, v_new, 1)
+    _check_attn(d, q, 1, n_q_heads, out, lse)
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     st = lib().wmtp_draft_step_windowed(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q),
                                         int(n_q_heads), float(sm_scale), _ptr(out), _ptr(lse),
@@ -303,9 +330,9 @@ def wmtp_draft_step_full(cache, k_new, v_new, q, n_q_heads: int, sm_scale: float
                          max_seq_len: int, out, lse, ws, ws_bytes: Optional[int] = None,
                          stream=None, check=True) -> int:
     """Append one token per sequence, then the full-context draft attention (one call)."""
-    _check_append(cache, k_new, v_new, 1)
-    _check_attn(cache, q, 1, n_q_heads, out, lse)
     d = _desc(cache)
+    _check_append(d, k_new, v_new, 1)
+    _check_attn(d, q, 1, n_q_heads, out, lse)
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     st = lib().wmtp_draft_step_full(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q),
                                     int(n_q_heads), float(sm_scale), int(max_seq_len), _ptr(out),
@@ -317,9 +344,9 @@ def wmtp_verify_step(cache, k_new, v_new, q, m: int, n_q_heads: int, sm_scale: f
                      max_seq_len: int, out, lse, ws, ws_bytes: Optional[int] = None, stream=None,
                      check=True) -> int:
     """Append the m candidates, then verify them (one call)."""
-    _check_append(cache, k_new, v_new, m)
-    _check_attn(cache, q, m, n_q_heads, out, lse)
     d = _desc(cache)
+    _check_append(d, k_new, v_new, m)
+    _check_attn(d, q, m, n_q_heads, out, lse)
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     st = lib().wmtp_verify_step(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q), int(m),
                                 int(n_q_heads), float(sm_scale), int(max_seq_len), _ptr(out),
@@ -330,8 +357,8 @@ def wmtp_verify_step(cache, k_new, v_new, q, m: int, n_q_heads: int, sm_scale: f
 def wmtp_draft_attn_masw(ring, slots, q, n_q_heads: int, sm_scale: float, max_slots: int, out,
                          lse, ws, ws_bytes: Optional[int] = None, stream=None, check=True) -> int:
     """MASW draft step: ring sinks + last W positions, plus memory slots 0..slots.seq_len[b]-1."""
-    _check_attn(ring, q, 1, n_q_heads, out, lse)
     r, sl = _desc(ring), _desc(slots)
+    _check_attn(r, q, 1, n_q_heads, out, lse)
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     st = lib().wmtp_draft_attn_masw(ctypes.byref(r), ctypes.byref(sl), _ptr(q), int(n_q_heads),
                                     float(sm_scale), int(max_slots), _ptr(out), _ptr(lse),

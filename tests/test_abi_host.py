@@ -266,3 +266,60 @@ def test_public_headers_compile(lang, tmp_path):
     r = subprocess.run([cc, "-fsyntax-only", "-Wall", "-Werror", "-I", inc, str(src)],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+# ------------------------------------------------------------------------------------------
+# the binding's cached cache descriptor (host logic; stand-in device tensors, no GPU)
+# ------------------------------------------------------------------------------------------
+class _DeviceTensor:
+    """Stands in for a dense device tensor: the binding reads only these attributes."""
+
+    def __init__(self, numel, elem_bytes, addr=FAKE, cuda=True, dense=True):
+        self._n, self._eb, self._addr = numel, elem_bytes, addr
+        self.is_cuda = cuda
+        self._dense = dense
+
+    def is_contiguous(self):
+        return self._dense
+
+    def data_ptr(self):
+        return self._addr
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return self._eb
+
+
+def _cache(batch=2, Hkv=2, d=128, cap=20, k=None):
+    rows = batch * Hkv * cap * d
+    return W.KVCache(k or _DeviceTensor(rows, 2), _DeviceTensor(rows, 2),
+                     _DeviceTensor(batch * cap, 4), _DeviceTensor(batch, 4), batch, Hkv, d, cap,
+                     4, 16, W.WMTP_BF16)
+
+
+def test_cache_descriptor_is_built_once_and_rebuilt_after_a_field_changes():
+    c = _cache()
+    d1 = c.desc()
+    assert c.desc() is d1  # reused while nothing changed
+    assert (d1.k, d1.batch, d1.capacity, d1.window) == (FAKE, 2, 20, 16)
+    c.k = _DeviceTensor(2 * 2 * 20 * 128, 2, addr=FAKE + 4096)
+    d2 = c.desc()
+    assert d2 is not d1 and d2.k == FAKE + 4096
+    c.window = 8
+    assert c.desc().window == 8
+
+
+def test_cache_descriptor_checks_the_cache_tensors():
+    with pytest.raises(ValueError, match="cache.k"):
+        _cache(k=_DeviceTensor(2 * 2 * 20 * 128 - 1, 2)).desc()  # one element short
+    with pytest.raises(ValueError, match="host tensor"):
+        _cache(k=_DeviceTensor(2 * 2 * 20 * 128, 2, cuda=False)).desc()
+    with pytest.raises(ValueError, match="dense"):
+        _cache(k=_DeviceTensor(2 * 2 * 20 * 128, 2, dense=False)).desc()
+    c = _cache()
+    c.desc()
+    c.seq_len = _DeviceTensor(1, 4)  # fewer lengths than sequences: refused at the rebuild
+    with pytest.raises(ValueError, match="seq_len"):
+        c.desc()

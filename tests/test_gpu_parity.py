@@ -326,6 +326,8 @@ def test_bytes_past_the_length_do_not_reach_results(dt, d):
     append_each(cache, K, V, [0] * B, lens)
     ring = W.KVCache.ring(B, Hkv, d, S, Wn, tdtype(dt))
     append_each(ring, K, V, [0] * B, lens)
+    slack = W.KVCache.ring(B, Hkv, d, S, Wn, tdtype(dt), slack=3)  # the masked-ring kernels
+    append_each(slack, K, V, [0] * B, lens)
     kn = torch.stack([K[b, :, lens[b]:lens[b] + 4].permute(1, 0, 2) for b in range(B)]).contiguous()
     vn = torch.stack([V[b, :, lens[b]:lens[b] + 4].permute(1, 0, 2) for b in range(B)]).contiguous()
     k1, v1 = kn[:, :1].contiguous(), vn[:, :1].contiguous()  # a draft step's token
@@ -350,10 +352,13 @@ def test_bytes_past_the_length_do_not_reach_results(dt, d):
                                bound, o, l, W.workspace(B, Hq, Hkv, d, m, bound))
         return o, l
 
-    # G = 4 (key-split kernel) and G = 16 with m = 4 (64 rows: cooperative kernel where it runs)
+    # G = 4 and 16 (key-split kernel), G = 32 or G = 16 with m = 4 (32 and 64 rows: cooperative
+    # kernel where it runs)
     cases = [(8, 1, "windowed", ring), (8, 1, "full", cache), (8, 1, "step_windowed", ring),
              (8, 1, "step_full", cache), (8, 4, "verify", cache), (32, 4, "verify", cache),
-             (32, 4, "verify_step", cache), (32, 1, "windowed", ring), (32, 1, "full", cache)]
+             (32, 4, "verify_step", cache), (32, 1, "windowed", ring), (32, 1, "full", cache),
+             (8, 1, "windowed", slack), (8, 1, "step_windowed", slack), (64, 1, "windowed", ring),
+             (64, 1, "windowed", slack)]
     for Hq, m, kind, base in cases:
         q = synth.queries(82, m, B, m, Hq, d, tdtype(dt), DEV)
         clean = W.KVCache(base.k.clone(), base.v.clone(),
@@ -365,3 +370,21 @@ def test_bytes_past_the_length_do_not_reach_results(dt, d):
         assert torch.isfinite(o1).all(), f"{kind} Hq={Hq} m={m}: non-finite output"
         assert torch.equal(o1, o2) and torch.equal(l1, l2), \
             f"{kind} Hq={Hq} m={m}: rows past the length changed the results"
+
+    # MASW step: ring (past each length) and memory-slot cache (past each slot count) both poisoned
+    counts, max_slots = [5, 9, 0], 64
+    Ks, Vs = logical_kv(83, B, Hkv, d, max(counts), tdtype(dt))
+    slots = W.KVCache.contiguous(B, Hkv, d, max_slots, tdtype(dt))
+    append_each(slots, Ks, Vs, [0] * B, counts)
+    for Hq, rb in ((8, ring), (8, slack), (64, ring)):
+        q = synth.queries(84, 0, B, 1, Hq, d, tdtype(dt), DEV)
+        res = []
+        for r_, s_ in ((rb, slots), (_poison(rb, lens), _poison(slots, counts))):
+            o = torch.full((B, 1, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
+            l = torch.full((B, 1, Hq), float("nan"), dtype=torch.float32, device=DEV)
+            W.wmtp_draft_attn_masw(r_, s_, q, Hq, 0.1, max_slots, o, l,
+                                   W.masw_workspace(B, Hq, Hkv, d, r_.capacity, max_slots))
+            res.append((o, l))
+        assert torch.isfinite(res[0][0]).all(), f"masw Hq={Hq}: non-finite output"
+        assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1]), \
+            f"masw Hq={Hq}: rows past the lengths changed the results"

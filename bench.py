@@ -337,6 +337,11 @@ def main():
             "verify_attn": round(gbs(b_ver, mean_us["ver_attn"]), 1),
             "windowed_attn_cold": None if win_cold is None else round(gbs(b_win, win_cold), 1),
         },
+        "hbm_frac_of_peak": {
+            "windowed_attn": round(gbs(b_win, mean_us["win_attn"]) / PEAK_HBM_GBS, 4),
+            "full_attn": round(gbs(b_full, mean_us["full_attn"]) / PEAK_HBM_GBS, 4),
+            "verify_attn": round(gbs(b_ver, mean_us["ver_attn"]) / PEAK_HBM_GBS, 4),
+        },
         "verify_us": {"attn": round(mean_us["ver_attn"], 2),
                       "attn_plus_append": round(mean_us["ver_step"], 2)},
         "dropped_kv_fraction": round(1.0 - win_slots / n_mid, 5),

@@ -113,3 +113,42 @@ def test_masw_slot_rollback_after_rejection():
     ro, rl = oracle.draft_masw(synth.host_array(q), ocode(dt), kv, [n0 + accepted], S, Wn,
                                synth.host_array(sk), synth.host_array(sv), [50], 0.125)
     compare(out, lse, ro, rl, dt, "masw after rollback")
+
+
+@pytest.mark.parametrize("r", [64, 8])
+def test_masw_million_token_context(r):
+    """The benchmark's MASW step at its size and launch configuration: the million-token draft
+    shapes (32 query / 2 KV heads, d 256, bf16, S 4, W 4096) at n = 1,048,577 with one memory slot
+    per r raw tokens (16,384 or 131,072 slots), every query head against the oracle."""
+    from draft_attention_amd import configs
+
+    wl = configs.MILLION
+    Hq, Hkv, d, S, Wn = wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.sink, wl.window
+    dt = torch.bfloat16
+    n = wl.context + 1
+    m = n // r
+    say(f"masw at n={n}, r={r}: {m} slots")
+    # the ring after n appends holds the sinks and the last W positions: append those only
+    ring = W.KVCache.ring(1, Hkv, d, S, Wn, dt)
+    Ks = torch.cat([synth.sequence_rows(wl.seed, synth.K_ID, 0, 0, S, Hkv, d, dt, DEV),
+                    synth.sequence_rows(wl.seed, synth.K_ID, 0, n - Wn, n, Hkv, d, dt, DEV)], dim=1)
+    Vs = torch.cat([synth.sequence_rows(wl.seed, synth.V_ID, 0, 0, S, Hkv, d, dt, DEV),
+                    synth.sequence_rows(wl.seed, synth.V_ID, 0, n - Wn, n, Hkv, d, dt, DEV)], dim=1)
+    tok = lambda X, r0, r1: X[:, r0:r1].permute(1, 0, 2).contiguous()[None]
+    W.wmtp_ring_append(ring, tok(Ks, 0, S), tok(Vs, 0, S), S)
+    ring.seq_len.fill_(n - Wn)
+    W.wmtp_ring_append(ring, tok(Ks, S, S + Wn), tok(Vs, S, S + Wn), Wn)
+    sk, sv = _slots(wl.seed + 3, 1, Hkv, d, m, "bf16")
+    slots = W.KVCache.contiguous(1, Hkv, d, m, dt)
+    for c0 in range(0, m, 1 << 16):
+        c1 = min(m, c0 + (1 << 16))
+        W.wmtp_ring_append(slots, sk[:, :, c0:c1].permute(0, 2, 1, 3).contiguous(),
+                           sv[:, :, c0:c1].permute(0, 2, 1, 3).contiguous(), c1 - c0)
+    q = synth.queries(wl.seed + 2, 0, 1, 1, Hq, d, dt, DEV)
+    scale = 1.0 / math.sqrt(d)
+    out, lse = _run(ring, slots, q, Hq, scale, m)
+    kv = oracle.LogicalKV(synth.host_array(Ks)[None], synth.host_array(Vs)[None], oracle.BF16,
+                          [[(0, 0, S), (n - Wn, S, Wn)]])
+    ro, rl = oracle.draft_masw(synth.host_array(q), oracle.BF16, kv, [n], S, Wn,
+                               synth.host_array(sk), synth.host_array(sv), [m], scale)
+    compare(out, lse, ro, rl, "bf16", f"masw at 1M, r={r}")

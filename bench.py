@@ -686,7 +686,8 @@ def sweep(W, synth, D3, full, cap, Hq, scale, probe_buf, probe_out, stream, ev, 
     lengths L (the step attends n = L + 1 tokens): windowed (ring holding sinks + window of the
     same sequence) and full (the first n rows of the contiguous cache), each timed per call with
     events after `warm_up` calls: cold (the caches flushed before every call) and warm (calls back
-    to back behind a backlog read); median, p10 and p90 of `calls` calls."""
+    to back behind a backlog read); median, p10 and p90 of `calls` calls. The one-call steps
+    (append, then attend) of both forms are timed the same way."""
     import torch
 
     dev = full.k.device
@@ -699,10 +700,13 @@ def sweep(W, synth, D3, full, cap, Hq, scale, probe_buf, probe_out, stream, ev, 
     ws_full = W.workspace(1, Hq, Hkv, d, 1, cap, dev)
     ws_win = W.workspace(1, Hq, Hkv, d, 1, S + Wn, dev)
     res = {"L": [], "n": [], "windowed_slots": [], "full_us_cold": [], "windowed_us_cold": [],
-           "full_us_warm": [], "windowed_us_warm": [], "full_gbs_cold": [],
-           "windowed_gbs_cold": [], "full_over_windowed_cold": []}
+           "full_us_warm": [], "windowed_us_warm": [], "full_step_us_cold": [],
+           "windowed_step_us_cold": [], "full_step_us_warm": [], "windowed_step_us_warm": [],
+           "full_gbs_cold": [], "windowed_gbs_cold": [], "full_over_windowed_cold": []}
     for L in SWEEP_L:
         n = L + 1
+        if n + warm_up + 2 * calls > cap:
+            raise ValueError("the contiguous cache has no room for the sweep's appended tokens")
         seq = torch.full((1,), n, dtype=torch.int32, device=dev)
         view = W.KVCache(full.k, full.v, None, seq, 1, Hkv, d, full.capacity, full.capacity, 0,
                          full.dtype)
@@ -715,9 +719,17 @@ def sweep(W, synth, D3, full, cap, Hq, scale, probe_buf, probe_out, stream, ev, 
             vn = synth.token_rows(D3.seed, synth.V_ID, 0, p0, p1, Hkv, d, dt, dev)[None]
             W.wmtp_ring_append(ring, kn, vn, p1 - p0)
         slots = min(n, S + Wn)
+        kn = synth.token_rows(D3.seed, synth.K_ID, 0, n, n + 1, Hkv, d, dt, dev)[None]
+        vn = synth.token_rows(D3.seed, synth.V_ID, 0, n, n + 1, Hkv, d, dt, dev)[None]
         calls_of = {
             "full": lambda: W.wmtp_draft_attn_full(view, q, Hq, scale, cap, out, lse, ws_full),
             "windowed": lambda: W.wmtp_draft_attn_windowed(ring, q, Hq, scale, out, lse, ws_win),
+            # the one-call steps (append, then attend; timing only): each call appends one more
+            # token, so the full read grows by one key per call (at most 2 * calls + warm_up)
+            "full_step": lambda: W.wmtp_draft_step_full(view, kn, vn, q, Hq, scale, cap, out, lse,
+                                                        ws_full),
+            "windowed_step": lambda: W.wmtp_draft_step_windowed(ring, kn, vn, q, Hq, scale, out,
+                                                                lse, ws_win),
         }
         for name, call in calls_of.items():
             for _ in range(warm_up):
@@ -756,7 +768,8 @@ def sweep(W, synth, D3, full, cap, Hq, scale, probe_buf, probe_out, stream, ev, 
         res["n"].append(n)
         res["windowed_slots"].append(slots)
         log(f"sweep L={L}: full {res['full_us_cold'][-1]['p50']} us, windowed "
-            f"{res['windowed_us_cold'][-1]['p50']} us (cold p50)")
+            f"{res['windowed_us_cold'][-1]['p50']} us (cold p50; steps "
+            f"{res['full_step_us_cold'][-1]['p50']} / {res['windowed_step_us_cold'][-1]['p50']} us)")
         del ring
     return res
 

@@ -313,6 +313,9 @@ int wmtp_ring_rollback(const wmtp_kv* cache, const int32_t* n_drop, void* stream
   int st = check_kv(cache);
   if (st != WMTP_OK) return st;
   if (!n_drop || !aligned(n_drop, 4)) return WMTP_ERR_INVALID_ARG;
+  // a ring's exact rollback depth is read from its position tags
+  if (cache->window >= 1 && cache->capacity - cache->sink - cache->window > 0 && !cache->pos)
+    return WMTP_ERR_INVALID_ARG;
   wmtp::RollbackArgs a;
   a.pos = cache->pos;
   a.seq_len = cache->seq_len;

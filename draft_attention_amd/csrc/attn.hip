@@ -1083,7 +1083,9 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, in
   float M = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   auto absorb = [&](float2 ml, float4 x) {
-    if (!(ml.y > 0.f)) return;  // empty partial
+    // an empty partial (no attended key: max -inf, sum 0) is skipped; a NaN partial is not, so a
+    // NaN among the attended keys reaches the output as it does in exact arithmetic
+    if (ml.y == 0.f) return;
     if (ml.x > M) {
       const float c = __builtin_amdgcn_exp2f(M - ml.x);  // 0 while M is -inf
       L *= c; acc.x *= c; acc.y *= c; acc.z *= c; acc.w *= c;
@@ -1153,13 +1155,13 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, in
     const float Lt = red_l[col];
     const float4 r = red_o[col];
     float4 res = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (Lt > 0.f) {
+    if (Lt != 0.f) {  // else nothing was attended: out = 0, lse = -inf (NaN propagates)
       const float inv = 1.f / Lt;
       res = make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
     }
     *reinterpret_cast<float4*>(a.out + (size_t)row_id * D + dim0 + col * 4) = res;
     if (col == 0 && blockIdx.y == 0 && a.lse)
-      a.lse[row_id] = (Lt > 0.f) ? (red_m[0] + log2f(Lt)) * kLn2 : -INFINITY;
+      a.lse[row_id] = (Lt != 0.f) ? (red_m[0] + log2f(Lt)) * kLn2 : -INFINITY;
   }
 }
 

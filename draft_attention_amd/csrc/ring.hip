@@ -114,15 +114,50 @@ __global__ __launch_bounds__(64) void append_bump_kernel(int32_t* seq_len, int b
   }
 }
 
-// Discard the newest n_drop[b] tokens of sequence b (clamped to [0, max_drop(n)]): the tags of
-// their slots become -1 and seq_len[b] shrinks. One workgroup per sequence; every thread reads seq_len[b]
-// before thread 0 changes it.
+// Deepest exact rollback of a ring (one wavefront, uniform result): the largest d <= d0 such
+// that the draft's attended set with n - d tokens present -- the sinks and the last W positions
+// -- is still held. Sinks are never overwritten, so only the oldest window position
+// q = max(S, n - d - W) has to be checked: the window positions still held form the run
+// [lo, n) (a slot loses position p only when position p + W + slack is appended, and positions
+// are appended in order), so q is held iff tag(slot(q)) == q, and that test passes for every d
+// up to some depth and fails beyond it. d with n - d <= S leaves sinks only and is always exact.
+// Each round tests 64 evenly spaced depths of the open range (one load per lane): depths <= 64
+// take one round.
+__device__ __forceinline__ int64_t exact_depth(const RollbackArgs& a, int b, int64_t n, int64_t d0) {
+  if (d0 <= 0 || n - d0 <= a.sink) return d0 < 0 ? 0 : d0;
+  const int lane = threadIdx.x;
+  const int attended = a.window - a.slack;
+  const int32_t* tags = a.pos + (size_t)b * a.capacity;
+  int64_t lo = 0, hi = d0;  // depth lo is exact (0: nothing dropped); the answer is in [lo, hi]
+  while (lo < hi) {
+    const int64_t step = (hi - lo + 63) / 64;
+    const int64_t c = lo + (int64_t)(lane + 1) * step;  // candidate depth of this lane
+    bool ok = false;
+    if (c <= hi) {
+      const int64_t q0 = n - c - attended;
+      const int64_t q = q0 > a.sink ? q0 : (int64_t)a.sink;
+      ok = tags[slot_of(q, a.sink, a.window)] == (int32_t)q;
+    }
+    const uint64_t pass = __ballot(ok);
+    const int j = __builtin_ctzll(~pass);  // lanes 0 .. j-1 passed
+    const int64_t lo_old = lo;
+    if (j > 0) lo = lo_old + (int64_t)j * step;
+    if (j < 64 && lo_old + (int64_t)(j + 1) * step <= hi) hi = lo_old + (int64_t)(j + 1) * step - 1;
+  }
+  return lo;
+}
+
+// Discard the newest n_drop[b] tokens of sequence b, clamped to [0, n] for a contiguous cache and
+// to the deepest exact rollback within [0, min(n, slack)] for a ring (exact_depth): the tags of
+// their slots become -1 and seq_len[b] shrinks. One wavefront per sequence; every lane reads
+// seq_len[b] before lane 0 changes it.
 __global__ __launch_bounds__(64) void rollback_kernel(RollbackArgs a) {
   const int b = blockIdx.x;
   const int64_t n = present(a.seq_len, b);
   int64_t d = a.n_drop[b];
   const int64_t cap = a.window == 0 ? n : (n < a.slack ? n : (int64_t)a.slack);
   d = d < 0 ? 0 : (d > cap ? cap : d);
+  if (a.window != 0) d = exact_depth(a, b, n, d);
   if (a.pos) {
     for (int64_t i = threadIdx.x; i < d; i += blockDim.x) {
       const int64_t p = n - d + i;

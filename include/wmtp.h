@@ -87,9 +87,10 @@ typedef enum wmtp_dtype { WMTP_F32 = 0, WMTP_BF16 = 1 } wmtp_dtype;
  * (INVALID_ARG otherwise).
  * A ring's window positions wrap over its capacity - sink window slots: slot(p) = p for p < sink,
  * else sink + (p - sink) % (capacity - sink). The draft attends the sinks and the last `window`
- * positions; the slack = capacity - sink - window extra slots let the newest `slack` tokens be
- * discarded again exactly (wmtp_ring_rollback), since every slot they overwrote held a position
- * older than the window that remains. slack = 0 is the compact ring of the Windowed-MTP abstract
+ * positions; the slack = capacity - sink - window extra slots let up to `slack` of the newest
+ * tokens be discarded again exactly (wmtp_ring_rollback), since every slot they overwrote held a
+ * position older than the window that remains (after an earlier rollback the exact depth can be
+ * smaller; see wmtp_ring_rollback). slack = 0 is the compact ring of the Windowed-MTP abstract
  * (last sentence). */
 typedef struct wmtp_kv {
   void* k;          /* device [batch][n_kv_heads][capacity][head_dim] */
@@ -191,13 +192,19 @@ size_t wmtp_masw_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_
 
 /* Discard the newest n_drop[b] tokens of every sequence b after a rejected speculation (the MASW
  * page, section 4.3: rejected speculative local KV is discarded). n_drop is device memory [batch],
- * typically written by wmtp_greedy_accept on the same stream. The count is clamped on the device
- * to [0, min(seq_len[b], slack)] for a ring and to [0, seq_len[b]] for a contiguous cache (a
- * contiguous cache overwrites nothing). The slots of the discarded positions get pos = -1 (when
- * pos is not NULL; positions at or past a contiguous cache's capacity have no slot), then
+ * typically written by wmtp_greedy_accept on the same stream. The count is clamped on the device:
+ * to [0, seq_len[b]] for a contiguous cache (which overwrites nothing), and for a ring to the
+ * largest d <= min(n_drop[b], seq_len[b], slack) after which every position the windowed draft
+ * attends (the sinks and the last `window` of the seq_len[b] - d that remain) is still held in its
+ * slot. Without earlier rollbacks that is min(n_drop[b], seq_len[b], slack); after a rollback,
+ * tokens appended again reuse the slots of the discarded ones while the older window slots they
+ * overwrote stay lost, so a second rollback deeper than what was appended since can be cut
+ * shorter. A ring's depth is read from the pos tags, so a ring with slack needs pos (INVALID_ARG
+ * otherwise), kept by the library's appends. The slots of the discarded positions get pos = -1
+ * (when pos is not NULL; positions at or past a contiguous cache's capacity have no slot), then
  * seq_len[b] shrinks by the count. K/V bytes are left as they are (no call reads them until a
- * later append overwrites them). Errors: INVALID_ARG (null or misaligned n_drop, bad descriptor),
- * UNSUPPORTED, HIP. */
+ * later append overwrites them). Errors: INVALID_ARG (null or misaligned n_drop, a ring with
+ * slack and no pos, bad descriptor), UNSUPPORTED, HIP. */
 int wmtp_ring_rollback(const wmtp_kv* cache, const int32_t* n_drop, void* stream);
 
 /* Greedy verification of k draft tokens per sequence from the target's logits (the target's

@@ -159,7 +159,8 @@ class RingModel:
     discarded), ``n[b]`` the number of tokens present. Window positions wrap over W + slack slots
     (slack = 0 is the compact ring of the abstract's last sentence); the draft attends the sinks and
     the last W positions only, so up to ``slack`` speculative tokens can be discarded again
-    (:meth:`rollback`) without having overwritten a position the window still needs. Appends are
+    (:meth:`rollback`) as long as no position the remaining window needs has been overwritten
+    (after earlier rollbacks, fewer: :meth:`exact_after`). Appends are
     applied token by token in position order, so a later token always overwrites an earlier one in
     the same slot.
     """
@@ -182,18 +183,40 @@ class RingModel:
         np.maximum.at(self.tags[b], s, p)
         self.n[b] += count
 
+    def exact_after(self, b: int, d: int) -> bool:
+        """Whether discarding the newest d tokens leaves an exact ring: every position that a
+        windowed draft step attends with n - d tokens present (the sinks and the last W) is still
+        held in its slot. A slot is overwritten by the position W + slack later, so after earlier
+        rollbacks a later append may already have taken a slot that a deeper rollback would need
+        again."""
+        if self.W < 1:
+            raise ValueError("only a ring (W >= 1) overwrites slots")
+        n = int(self.n[b]) - d
+        for a, c in windowed_positions(n, self.S, self.W):
+            for p in range(a, c):
+                if self.tags[b, ring_slot(p, self.S, self.Wp)] != p:
+                    return False
+        return True
+
     def max_rollback(self, b: int) -> int:
-        """How many of the newest tokens can be discarded exactly: the slack (every slot that a
-        discarded token overwrote held a position older than the window that remains); all of them
-        for a contiguous cache (W = 0, nothing is ever overwritten)."""
+        """The largest number of newest tokens that can be discarded exactly: at most the slack,
+        and only as deep as :meth:`exact_after` allows (all of them for a contiguous cache, W = 0,
+        which overwrites nothing)."""
+        return self._clamp(b, int(self.n[b]))
+
+    def _clamp(self, b: int, count: int) -> int:
+        n = int(self.n[b])
         if self.W == 0:
-            return int(self.n[b])
-        return int(min(self.n[b], self.slack))
+            return max(0, min(count, n))
+        d = max(0, min(count, n, self.slack))
+        while d > 0 and not self.exact_after(b, d):
+            d -= 1
+        return d
 
     def rollback(self, b: int, count: int) -> int:
-        """Discard the newest ``count`` tokens (clamped to [0, max_rollback]): their slots are
-        marked empty and n shrinks. Returns how many were discarded."""
-        d = int(max(0, min(count, self.max_rollback(b))))
+        """Discard the newest tokens: the largest d <= count (and <= the slack) that leaves an
+        exact ring (:meth:`exact_after`). Their slots are marked empty and n shrinks. Returns d."""
+        d = self._clamp(b, int(count))
         if d:
             p = np.arange(self.n[b] - d, self.n[b], dtype=np.int64)
             self.tags[b, ring_slot(p, self.S, self.Wp)] = -1

@@ -163,6 +163,8 @@ def test_rollback_arguments_rejected_before_launch(lib):
     assert L.wmtp_ring_rollback(ctypes.byref(_kv()), None, None) == W.WMTP_ERR_INVALID_ARG
     assert L.wmtp_ring_rollback(ctypes.byref(_kv()), FAKE + 2, None) == W.WMTP_ERR_INVALID_ARG
     assert L.wmtp_ring_rollback(ctypes.byref(_kv(head_dim=96)), FAKE, None) == W.WMTP_ERR_UNSUPPORTED
+    # a ring with slack reads its exact rollback depth from the position tags: pos is required
+    assert L.wmtp_ring_rollback(ctypes.byref(_kv(capacity=24)), FAKE, None) == W.WMTP_ERR_INVALID_ARG
 
 
 def test_accept_arguments_rejected_before_launch(lib):

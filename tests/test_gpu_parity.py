@@ -388,3 +388,54 @@ def test_bytes_past_the_length_do_not_reach_results(dt, d):
         assert torch.isfinite(res[0][0]).all(), f"masw Hq={Hq}: non-finite output"
         assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1]), \
             f"masw Hq={Hq}: rows past the lengths changed the results"
+
+
+# ------------------------------------------------------------------------------------------
+# a NaN INSIDE the attended set reaches the results (as in exact arithmetic): the merge must not
+# drop the partial that holds it and keep a finite, wrong result built from the other partials
+# ------------------------------------------------------------------------------------------
+def _compare_nan(out, lse, ref_out, ref_lse, dt, what):
+    o = out.double().cpu().numpy()
+    l = lse.double().cpu().numpy()
+    assert np.array_equal(np.isnan(o), np.isnan(ref_out)), f"{what}: NaN outputs differ"
+    assert np.array_equal(np.isnan(l), np.isnan(ref_lse)), f"{what}: NaN lse differ"
+    assert np.isnan(ref_out).any(), f"{what}: the planted NaN did not reach the oracle"
+    ok = ~np.isnan(ref_out)
+    err = float(np.max(np.abs(o[ok] - ref_out[ok])))
+    okl = np.isfinite(ref_lse)
+    lerr = float(np.max(np.abs(l[okl] - ref_lse[okl])))
+    say(f"  {what}: NaN pattern equal; elsewhere max|out-ref| = {err:.3e} lse {lerr:.3e}")
+    assert err <= TOL[dt] and lerr <= TOL[dt], what
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("bf16", 256), ("f32", 64)])
+def test_nan_inside_the_attended_set_propagates(dt, d):
+    """One K row (sequence 0, KV head 0) and one V element (sequence 1, KV head 1) hold NaN at
+    attended positions: exactly the outputs the oracle makes NaN are NaN (the whole query group
+    for the K row, one dimension for the V element), on the key-split kernel (windowed ring, full
+    draft) and the cooperative kernel (verification, a 32-head group)."""
+    B, Hkv, S, Wn, n, bound = 2, 2, 4, 64, 700, 1024
+    say(f"NaN inside the attended set: {dt} d={d}")
+    K, V = logical_kv(85, B, Hkv, d, n, tdtype(dt))
+    K[0, 0, n - 3] = float("nan")           # a window position (also seen by the full read)
+    V[1, 1, n - 10, d // 2 + 1] = float("nan")
+    kv = oracle_kv(K, V, dt)
+    cache = W.KVCache.contiguous(B, Hkv, d, bound, tdtype(dt))
+    append_each(cache, K, V, [0] * B, [n] * B)
+    ring = W.KVCache.ring(B, Hkv, d, S, Wn, tdtype(dt))
+    append_each(ring, K, V, [0] * B, [n] * B)
+    scale = 1.0 / math.sqrt(d)
+    for Hq in (16, 64):
+        q = synth.queries(86, Hq, B, 1, Hq, d, tdtype(dt), DEV)
+        qh = synth.host_array(q)
+        o, l = run_windowed(ring, q, Hq, scale)
+        ro, rl = oracle.draft_windowed(qh, ocode(dt), kv, [n] * B, S, Wn, scale)
+        _compare_nan(o, l, ro, rl, dt, f"windowed Hq={Hq}")
+        o, l = run_full(cache, q, Hq, scale, bound)
+        ro, rl = oracle.draft_full(qh, ocode(dt), kv, [n] * B, scale)
+        _compare_nan(o, l, ro, rl, dt, f"full Hq={Hq}")
+    for Hq, m in ((16, 4), (8, 2)):
+        q = synth.queries(87, m, B, m, Hq, d, tdtype(dt), DEV)
+        o, l = run_verify(cache, q, Hq, scale, bound)
+        ro, rl = oracle.verify(synth.host_array(q), ocode(dt), kv, [n] * B, scale)
+        _compare_nan(o, l, ro, rl, dt, f"verify Hq={Hq} m={m}")

@@ -25,6 +25,8 @@ def _check_ring(ring: W.KVCache, model: oracle.RingModel, seq_k, seq_v, what: st
     assert np.array_equal(ring.seq_len.cpu().numpy().astype(np.int64), model.n), f"{what}: seq_len"
     hk, hv = synth.host_array(ring.k), synth.host_array(ring.v)
     for b in range(ring.batch):
+        if ring.window >= 1:
+            model.attended_slots(b)  # raises if the model lost a position the window needs
         occ = model.occupied_slots(b)
         pos = model.tags[b, occ]
         assert np.array_equal(hk[b][:, occ], seq_k[b][:, pos]), f"{what}: K bytes of sequence {b}"
@@ -71,8 +73,7 @@ class _Spec:
     def rollback(self, drops):
         W.wmtp_ring_rollback(self.ring, torch.tensor(drops, dtype=torch.int32, device=DEV))
         for b, d in enumerate(drops):
-            expect = min(max(int(d), 0), self.model.max_rollback(b))
-            assert self.model.rollback(b, int(d)) == expect
+            self.model.rollback(b, int(d))  # the depth the device must have taken
             n = int(self.model.n[b])
             self.seq_k[b] = self.seq_k[b][:, :n]
             self.seq_v[b] = self.seq_v[b][:, :n]
@@ -131,6 +132,33 @@ def test_windowed_attention_after_rollbacks(dt, G, d):
         spec.rollback(rng.integers(0, k + 1, size=B).tolist())
         spec.append(1)  # the target's correction / bonus token
     _check_ring(spec.ring, spec.model, spec.seq_k, spec.seq_v, "end of loop")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("S,Wn,slack", [(4, 7, 3), (0, 7, 3), (2, 16, 9)])
+def test_rollback_deeper_than_the_last_append(dt, S, Wn, slack):
+    """Rollbacks that ask for more than was appended since the previous one (the device must stop
+    where a later append overwrote a window slot): after each, the tags and bytes equal the host
+    model's and the windowed read equals the oracle over the logical sequence."""
+    B, Hkv, d, G = 3, 2, 128, 8
+    Hq = G * Hkv
+    say(f"deep rollbacks {dt} S={S} W={Wn} slack={slack}")
+    spec = _Spec(B, Hkv, d, S, Wn, slack, dt, seed=53)
+    rng = np.random.default_rng(S * 100 + Wn + slack)
+    scale = 1.0 / math.sqrt(d)
+    ws = W.workspace(B, Hq, Hkv, d, 1, spec.ring.capacity)
+    spec.append(19)
+    for step in range(16):
+        spec.append(int(rng.integers(1, 3)))
+        spec.rollback([slack, int(rng.integers(0, slack + 3)), slack + 1])
+        _check_ring(spec.ring, spec.model, spec.seq_k, spec.seq_v, f"step {step}")
+        q = synth.queries(97, step, B, 1, Hq, d, tdtype(dt), DEV)
+        out = torch.empty((B, 1, Hq, d), dtype=torch.float32, device=DEV)
+        lse = torch.empty((B, 1, Hq), dtype=torch.float32, device=DEV)
+        W.wmtp_draft_attn_windowed(spec.ring, q, Hq, scale, out, lse, ws)
+        ro, rl = oracle.draft_windowed(synth.host_array(q), ocode(dt), spec.logical_kv(),
+                                       spec.model.n.tolist(), S, Wn, scale)
+        compare(out, lse, ro, rl, dt, f"step {step}")
 
 
 def _logits(B, k, V, dt, seed, ties=True):

@@ -49,6 +49,8 @@ MUTATIONS = [
     ("rollback leaves tags in place", "__init__.py",
      "self.tags[b, ring_slot(p, self.S, self.Wp)] = -1",
      "self.tags[b, ring_slot(p, self.S, self.Wp)] += 0", 1),
+    ("rollback clamped to the slack alone", "__init__.py",
+     "while d > 0 and not self.exact_after(b, d):", "while False:", 1),
     ("ties go to the highest index", "__init__.py",
      "choice = np.argmax(logits, axis=2).astype(np.int64)",
      "choice = (logits.shape[2] - 1 - np.argmax(logits[:, :, ::-1], axis=2)).astype(np.int64)", 1),

@@ -491,6 +491,69 @@ def test_rollback_is_clamped_to_the_slack_and_marks_slots_empty():
     assert flat.tags[0, :3].tolist() == [0, 1, 2] and (flat.tags[0, 3:] == -1).all()
 
 
+def test_second_rollback_stops_where_the_window_was_overwritten():
+    """A rollback deeper than what was appended since the previous one: with W = 7 and slack = 3
+    after 19 appends, append 1 and discard 3 (n = 17), then append 1 and ask for 3 again. The
+    first append wrote position 19 over position 9 and the second wrote position 17 back into its
+    own slot, so n may only go back to 17 (the window 10..16 is held; 8..9 are not): the second
+    rollback discards 1 token, not 3."""
+    for S in (0, 2):
+        model = oracle.RingModel(1, S, 7, 3)
+        model.append(0, 19)
+        model.append(0, 1)
+        assert model.rollback(0, 3) == 3 and model.n[0] == 17
+        model.append(0, 1)
+        assert model.rollback(0, 3) == 1 and model.n[0] == 17
+        expect = list(range(min(S, 17))) + list(range(max(S, 10), 17))
+        assert _attended_positions(model) == expect
+
+
+def _replay_held(ops, S, W, slack):
+    """Positions held after a log of ('append', count) / ('drop', d) operations, replayed token by
+    token into a dict slot -> position (a slot keeps the last position written to it; a dropped
+    position's slot is emptied)."""
+    slots, n = {}, 0
+    for op, c in ops:
+        if op == "append":
+            for p in range(n, n + c):
+                slots[p if p < S else S + (p - S) % (W + slack)] = p
+            n += c
+        else:
+            for p in range(n - c, n):
+                slots.pop(p if p < S else S + (p - S) % (W + slack), None)
+            n -= c
+    return set(slots.values()), n
+
+
+@pytest.mark.parametrize("S,W,slack", [(4, 8, 3), (0, 5, 5), (1, 1, 2), (3, 16, 9), (2, 3, 12)])
+def test_rollback_depth_is_the_deepest_that_keeps_the_window(S, W, slack):
+    """Rollbacks of any requested depth, deeper than the last append included: the depth the model
+    takes is the largest d <= min(request, n, slack) for which every position of the remaining
+    sinks + last-W set is held, where 'held' comes from replaying the whole operation log into a
+    plain slot dictionary (no ring model)."""
+    rng = np.random.default_rng(S * 1000 + W * 10 + slack + 1)
+    model = oracle.RingModel(1, S, W, slack)
+    ops = []
+    for step in range(80):
+        c = int(rng.integers(1, slack + 3))
+        model.append(0, c)
+        ops.append(("append", c))
+        req = int(rng.integers(-1, slack + 4))
+        held, n = _replay_held(ops, S, W, slack)
+
+        def keeps(d):
+            need = set(range(min(S, n - d))) | set(range(max(S, n - d - W), n - d))
+            return need <= held
+
+        cap = max(0, min(req, n, slack))
+        want = max(d for d in range(cap + 1) if keeps(d))
+        got = model.rollback(0, req)
+        assert got == want, (step, n, req)
+        ops.append(("drop", got))
+        assert _attended_positions(model) == sorted(
+            set(range(min(S, n - got))) | set(range(max(S, n - got - W), n - got)))
+
+
 def test_rollback_then_reappend_attends_the_replacement_tokens(oracle_lib):
     """Speculative loop on real rows: drafts are appended, some rejected and replaced by other
     tokens at the same positions. Attention over the ring's attended slots equals windowed

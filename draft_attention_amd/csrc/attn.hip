@@ -141,13 +141,14 @@ __device__ __forceinline__ void load_tile(const char* kbase, const char* vbase, 
 
 // The query operand of S^T = K . Q^T for this lane: fragment (rb, ks) holds row rb*16 + (lane & 15),
 // dims ks*32 + (lane >> 4)*8 .. +7 (bf16) or ks*16 + (lane >> 4)*4 .. +3 (fp32). It lives either in
-// registers or, when it would crowd out the K/V tiles, in LDS (read back once per tile; consecutive
-// lanes read consecutive 16 bytes, so the reads are conflict-free).
-template <int D, int NR, bool BF16>
+// registers or in LDS (read back once per tile; consecutive lanes read consecutive 16 bytes, so the
+// reads are conflict-free): in LDS when it would crowd out the K/V tiles, or when FORCE_LDS asks
+// for one load per workgroup instead of one per wavefront (short reads, see the planner).
+template <int D, int NR, bool BF16, bool FORCE_LDS = false>
 struct QOperand {
   using F = Frag<D, BF16>;
   typedef typename std::conditional<BF16, bf16x8_t, f32x4_t>::type Vec;
-  static constexpr bool kInLds = NR * F::kQRegs * 4 >= 64;
+  static constexpr bool kInLds = FORCE_LDS || NR * F::kQRegs * 4 >= 64;
   Vec reg[kInLds ? 1 : NR][kInLds ? 1 : F::kQRegs];
   const uint4* lds;
   int lane;
@@ -200,14 +201,10 @@ __device__ __forceinline__ RingMask ring_mask(const AttnArgs& a, int raw_n) {
   return r;
 }
 
-template <int D, int NR, bool BF16, bool RING>
-__device__ __forceinline__ void compute_tile(const Tile<D, BF16>& T, const QOperand<D, NR, BF16>& qf,
-                                             int t0, int last, const int (&last_visible)[NR],
-                                             const RingMask& rm, int grp, float scale_log2,
-                                             RowState<D, NR, BF16>& st) {
+// S^T = K_tile . Q^T of one tile (the score products; they do not depend on the running state)
+template <int D, int NR, bool BF16, typename QOp>
+__device__ __forceinline__ void tile_scores(const Tile<D, BF16>& T, const QOp& qf, f32x4_t (&s)[NR]) {
   using F = Frag<D, BF16>;
-  // ---------------- S^T = K_tile . Q^T
-  f32x4_t s[NR];
 #pragma unroll
   for (int rb = 0; rb < NR; ++rb) s[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if constexpr (BF16) {
@@ -231,7 +228,15 @@ __device__ __forceinline__ void compute_tile(const Tile<D, BF16>& T, const QOper
       }
     }
   }
+}
 
+// The online-softmax update of the running state with one tile whose scores s are given.
+template <int D, int NR, bool BF16, bool RING>
+__device__ __forceinline__ void tile_update(const Tile<D, BF16>& T, const f32x4_t (&s)[NR], int t0,
+                                            int last, const int (&last_visible)[NR],
+                                            const RingMask& rm, int grp, float scale_log2,
+                                            RowState<D, NR, BF16>& st) {
+  using F = Frag<D, BF16>;
   // ---------------- online softmax; this lane holds keys t0 + 4*grp + j (j = 0..3) of its row.
   // The weights are taken relative to a reference maximum st.m that only moves when a tile's
   // maximum exceeds it by more than kRescaleLog2 (softmax does not depend on the reference), so
@@ -335,6 +340,16 @@ __device__ __forceinline__ void compute_tile(const Tile<D, BF16>& T, const QOper
   }
 }
 
+template <int D, int NR, bool BF16, bool RING, typename QOp>
+__device__ __forceinline__ void compute_tile(const Tile<D, BF16>& T, const QOp& qf, int t0,
+                                             int last, const int (&last_visible)[NR],
+                                             const RingMask& rm, int grp, float scale_log2,
+                                             RowState<D, NR, BF16>& st) {
+  f32x4_t s[NR];
+  tile_scores<D, NR, BF16>(T, qf, s);
+  tile_update<D, NR, BF16, RING>(T, s, t0, last, last_visible, rm, grp, scale_log2, st);
+}
+
 // Lane (r16, grp) holds O^T rows 4*grp + j of every 16-dim block; block sx*kDpl + u covers
 // dims sx*kSetDims + kDpl*(4*grp + j) + u. These are four runs of kDpl contiguous dims per set.
 template <int D, bool BF16>
@@ -371,7 +386,8 @@ constexpr bool pipelined() {
   return q + o + 2 * tile <= 224 && o <= 96;
 }
 
-template <int D, int NR, bool BF16, bool RING, bool FUSED>
+// QLDS: the query operand is loaded once per workgroup and read from LDS (short reads).
+template <int D, int NR, bool BF16, bool RING, bool FUSED, bool QLDS>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_splits,
                                                               int n_chunks, int chunk_rows) {
   using F = Frag<D, BF16>;
@@ -406,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   // ---- query rows of this lane: row = row0 + rb*16 + r16 -> candidate jq, head hq. The query
   // loads go out first, ahead of the first tile: every later wait for a tile then also covers
   // them, on the first pass through the tile loop as on the others.
-  using QOp = QOperand<D, NR, BF16>;
+  using QOp = QOperand<D, NR, BF16, QLDS>;
   static_assert(!QOp::kInLds || NR <= kWavesPerBlock, "one row block per wavefront for the LDS copy");
   __shared__ uint4 sm_q[QOp::kInLds ? NR * F::kQRegs * 64 : 1];
   int row_j[NR];  // candidate index of the row
@@ -471,14 +487,15 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
       fresh = (int)slot;
       if (split == 0 && chunk == 0) {  // one workgroup per KV head stores the token
         constexpr int kPieces = D * F::kEB / 16;
-        const int i = threadIdx.x;
-        if (i < kPieces)
-          reinterpret_cast<uint4*>(const_cast<char*>(kbase) + (size_t)slot * D * F::kEB)[i] =
-              reinterpret_cast<const uint4*>(knew)[i];
-        else if (i < 2 * kPieces)
-          reinterpret_cast<uint4*>(const_cast<char*>(vbase) + (size_t)slot * D * F::kEB)[i - kPieces] =
-              reinterpret_cast<const uint4*>(vnew)[i - kPieces];
-        if (h == 0 && i == 0 && a.pos) a.pos[(size_t)b * a.capacity + slot] = (int32_t)p;
+        for (int i = threadIdx.x; i < 2 * kPieces; i += kThreads) {
+          if (i < kPieces)
+            reinterpret_cast<uint4*>(const_cast<char*>(kbase) + (size_t)slot * D * F::kEB)[i] =
+                reinterpret_cast<const uint4*>(knew)[i];
+          else
+            reinterpret_cast<uint4*>(const_cast<char*>(vbase) + (size_t)slot * D * F::kEB)[i - kPieces] =
+                reinterpret_cast<const uint4*>(vnew)[i - kPieces];
+        }
+        if (h == 0 && threadIdx.x == 0 && a.pos) a.pos[(size_t)b * a.capacity + slot] = (int32_t)p;
       }
     }
     n = n < 0x7fffffff ? n + 1 : n;
@@ -1174,20 +1191,29 @@ hipError_t launch_split(const AttnArgs& a, const SplitPlan& p, hipStream_t strea
   if (p.nr < 1 || p.nr > kMaxNr) return hipErrorInvalidValue;
   const bool ring = ring_masked(a);
   const bool fused = a.new_k != nullptr;
+  if (p.q_lds && p.nr != 1) return hipErrorInvalidValue;  // planned for one row block only
+#define WMTP_SPLIT1(RINGV, FUSEDV)                                                                      \
+  do {                                                                                                 \
+    if (p.q_lds)                                                                                       \
+      attn_split_kernel<D, 1, BF16, RINGV, FUSEDV, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); \
+    else                                                                                               \
+      attn_split_kernel<D, 1, BF16, RINGV, FUSEDV, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); \
+  } while (0)
   if (ring || fused) {
     // draft steps have one query token: G <= 16 rows, one row block
     if (p.nr != 1) return hipErrorInvalidValue;
-    if (ring && fused) attn_split_kernel<D, 1, BF16, true, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
-    else if (ring) attn_split_kernel<D, 1, BF16, true, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
-    else attn_split_kernel<D, 1, BF16, false, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows);
+    if (ring && fused) WMTP_SPLIT1(true, true);
+    else if (ring) WMTP_SPLIT1(true, false);
+    else WMTP_SPLIT1(false, true);
   } else {
     switch (p.nr) {
-      case 1: attn_split_kernel<D, 1, BF16, false, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
-      case 2: if constexpr (kMaxNr >= 2) attn_split_kernel<D, 2, BF16, false, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
-      case 3: if constexpr (kMaxNr >= 3) attn_split_kernel<D, 3, BF16, false, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
-      default: if constexpr (kMaxNr >= 4) attn_split_kernel<D, 4, BF16, false, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+      case 1: WMTP_SPLIT1(false, false); break;
+      case 2: if constexpr (kMaxNr >= 2) attn_split_kernel<D, 2, BF16, false, false, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+      case 3: if constexpr (kMaxNr >= 3) attn_split_kernel<D, 3, BF16, false, false, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
+      default: if constexpr (kMaxNr >= 4) attn_split_kernel<D, 4, BF16, false, false, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); break;
     }
   }
+#undef WMTP_SPLIT1
   return hipGetLastError();
 }
 
@@ -1276,6 +1302,12 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
   if (per > cap_per) per = cap_per;
   if (per < 1) per = 1;
   p->n_splits = (int)per;
+  // A short read (the windowed draft step: a few thousand keys per KV head) fills fewer workgroups
+  // than the target, each of about one tile per wavefront; it is latency-bound. Its query operand
+  // is loaded once per workgroup into LDS instead of once per wavefront: measured on MI355X at the
+  // million-token draft shapes, a quarter fewer bytes through each CU's address unit bring the
+  // tiles in 0.8 us earlier (windowed call 9.65 -> 9.2 us, graph-replayed).
+  p->q_lds = !p->coop && p->nr == 1 && bhc * cap_per < target_blocks;
   p->ws_o_floats = (size_t)bhc * p->n_splits * 16 * p->nr * head_dim;
   p->ws_ml_floats = (size_t)bhc * p->n_splits * 16 * p->nr * 2;
   return true;

@@ -21,6 +21,7 @@ struct SplitPlan {
   bool coop;           // cooperative-tile kernel (else the key-split kernel)
   int nr;              // 16-row MFMA blocks per chunk
   int n_splits;        // workgroups (partials) per (sequence, KV head, chunk)
+  bool q_lds;          // key-split kernel: query operand loaded once per workgroup into LDS
   size_t ws_o_floats;  // partial outputs: [bhc][n_splits][16*nr][head_dim]
   size_t ws_ml_floats; // running max and sum: [bhc][n_splits][16*nr][2]
 };

@@ -66,6 +66,10 @@ __device__ __forceinline__ void request_args(const AttnArgs& a) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+__device__ __forceinline__ unsigned div_of(unsigned x, const FastDiv& f) {
+  return (__umulhi(x, f.mul) + x) >> f.shift;
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.f;  // softmax weights stay below 2^8 between rescales
@@ -403,12 +407,12 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x;
   const int bhc = blockIdx.y;
-  // (unsigned divisions: every operand is nonnegative, and their sequences are shorter)
-  const int chunk = (unsigned)bhc % (unsigned)n_chunks;
-  const int bh = (unsigned)bhc / (unsigned)n_chunks;
-  const int h = (unsigned)bh % (unsigned)a.n_kv_heads;
-  const int b = (unsigned)bh / (unsigned)a.n_kv_heads;
-  const int G = (unsigned)a.n_q_heads / (unsigned)a.n_kv_heads;
+  // (divisions by the call's invariant sizes as multiply-shifts: every operand is below 2^31)
+  const int bh = div_of(bhc, a.div_chunks);
+  const int chunk = bhc - bh * n_chunks;
+  const int b = div_of(bh, a.div_kv);
+  const int h = bh - b * a.n_kv_heads;
+  const int G = a.div_g.d;
   const int rows = G * a.m;
   const int row0 = chunk * chunk_rows;
   const int row_end = min(rows, row0 + chunk_rows);
@@ -437,8 +441,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
     row_ok[rb] = row < row_end;
     // padding rows load the last real row (never written out; no select, so no early wait)
     const int row_q = row_ok[rb] ? row : row_end - 1;
-    const int jq = (unsigned)row_q / (unsigned)G;
-    const int hq = h * G + (unsigned)row_q % (unsigned)G;
+    const int jq = div_of(row_q, a.div_g);
+    const int hq = h * G + (row_q - jq * G);
     row_j[rb] = jq;
     if (QOp::kInLds && rb != wave) continue;  // LDS copy: one wave per row block
     const size_t qoff = ((size_t)(b * a.m + jq) * a.n_q_heads + hq) * D;
@@ -709,12 +713,12 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   const int d0 = (wave % C::kSplitD) * C::kDw;
   const int split = blockIdx.x;
   const int bhc = blockIdx.y;
-  // (unsigned divisions: every operand is nonnegative, and their sequences are shorter)
-  const int chunk = (unsigned)bhc % (unsigned)n_chunks;
-  const int bh = (unsigned)bhc / (unsigned)n_chunks;
-  const int h = (unsigned)bh % (unsigned)a.n_kv_heads;
-  const int b = (unsigned)bh / (unsigned)a.n_kv_heads;
-  const int G = (unsigned)a.n_q_heads / (unsigned)a.n_kv_heads;
+  // (divisions by the call's invariant sizes as multiply-shifts: every operand is below 2^31)
+  const int bh = div_of(bhc, a.div_chunks);
+  const int chunk = bhc - bh * n_chunks;
+  const int b = div_of(bh, a.div_kv);
+  const int h = bh - b * a.n_kv_heads;
+  const int G = a.div_g.d;
   const int rows = G * a.m;
   const int row_end = min(rows, chunk * chunk_rows + chunk_rows);
   const int r16 = lane & 15;
@@ -737,8 +741,8 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
     const int row = chunk * chunk_rows + (rb0 + kWavesPerBlock * j) * 16 + r16;
     row_ok[j] = row < row_end;
     const int row_q = row_ok[j] ? row : row_end - 1;
-    const int jq = (unsigned)row_q / (unsigned)G;
-    const int hq = h * G + (unsigned)row_q % (unsigned)G;
+    const int jq = div_of(row_q, a.div_g);
+    const int hq = h * G + (row_q - jq * G);
     row_j[j] = jq;
     const size_t qoff = ((size_t)(b * a.m + jq) * a.n_q_heads + hq) * D;
 #pragma unroll
@@ -1053,36 +1057,36 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
 
 // One workgroup per (output row, 4*COLS dims). COLS threads cover the dims as float4 columns;
 // 256/COLS lanes of splits stride over the partials in one online pass (each lane keeps its own
-// running max and rescales), a batch of COLS independent loads per lane covering 256 splits; the
-// lanes then combine with the same rescaling rule, by shuffles inside each wavefront and through
-// LDS across the four. Measured on MI355X: 8 columns (twice the workgroups, half the loads per
+// running max and rescales), a batch of BATCH independent loads per lane (sized to the split
+// count, up to 256 splits in one batch); the lanes then combine with the same rescaling rule, by
+// shuffles inside each wavefront and through LDS across the four. Measured on MI355X: 8 columns (twice the workgroups, half the loads per
 // lane) are as fast or faster up to 256 splits per row (the draft steps' 65-128, verification's
 // 256); 16 columns take larger split counts in one batch.
-template <int D, int COLS>
+template <int D, int COLS, int BATCH>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, int n_chunks,
                                                     int chunk_rows, int nr) {
   constexpr int kCols = COLS;
   constexpr int kSplitLanes = 256 / kCols;
-  constexpr int kBatch = COLS;
+  constexpr int kBatch = BATCH;
   __shared__ float red_m[256];
   __shared__ float4 red_o[256];
   __shared__ float red_l[256];
   request_args(a);
 
-  // index arithmetic in unsigned ints (all values are nonnegative; the unsigned divisions are
-  // shorter instruction sequences than the signed ones)
+  // index arithmetic in unsigned ints (all values are nonnegative), divisions by the call's
+  // invariant sizes as multiply-shifts
   const unsigned row_id = blockIdx.x;  // ((b * m + j) * Hq + hq)
   const int dim0 = blockIdx.y * (4 * kCols);
   const unsigned nq = a.n_q_heads, nkv = a.n_kv_heads, um = a.m, crows = chunk_rows;
-  const unsigned hq = row_id % nq;
-  const unsigned bj = row_id / nq;
-  const unsigned j = bj % um;
-  const unsigned b = bj / um;
-  const unsigned G = nq / nkv;
-  const unsigned h = hq / G;
-  const unsigned row = j * G + (hq % G);
-  const unsigned chunk = row / crows;
-  const int rloc = row % crows;
+  const unsigned bj = div_of(row_id, a.div_hq);
+  const unsigned hq = row_id - bj * nq;
+  const unsigned b = div_of(bj, a.div_m);
+  const unsigned j = bj - b * um;
+  const unsigned G = a.div_g.d;
+  const unsigned h = div_of(hq, a.div_g);
+  const unsigned row = j * G + (hq - h * G);
+  const unsigned chunk = div_of(row, a.div_crows);
+  const int rloc = row - chunk * crows;
   const size_t base = ((size_t)(b * nkv + h) * n_chunks + chunk) * n_splits;
   const int rows16 = 16 * nr;
   const int tid = threadIdx.x;
@@ -1313,19 +1317,39 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
   return true;
 }
 
+// The kernels' divisors for the sizes of `a` and the plan.
+static AttnArgs with_divisors(const AttnArgs& a, const SplitPlan& p) {
+  AttnArgs b = a;
+  b.div_hq = make_fastdiv(a.n_q_heads);
+  b.div_kv = make_fastdiv(a.n_kv_heads);
+  b.div_g = make_fastdiv(a.n_q_heads / a.n_kv_heads);
+  b.div_m = make_fastdiv(a.m);
+  b.div_chunks = make_fastdiv(p.n_chunks);
+  b.div_crows = make_fastdiv(p.chunk_rows);
+  return b;
+}
+
 template <int D>
 hipError_t launch_merge(const AttnArgs& a, const SplitPlan& p, int total_splits, hipStream_t stream) {
   const unsigned rows = a.batch * a.m * a.n_q_heads;
+  // loads per split lane sized to the split count (a lane's slots past the last split would only
+  // re-read it): 8 columns x 32 split lanes x 1-8 loads up to 256 splits, 16 x 16 x 16 beyond
+  const dim3 g8(rows, D / 32), g16(rows, D / 64), blk(256);
   if (total_splits > 256)
-    merge_kernel<D, 16><<<dim3(rows, D / 64), dim3(256), 0, stream>>>(a, total_splits, p.n_chunks,
-                                                                     p.chunk_rows, p.nr);
+    merge_kernel<D, 16, 16><<<g16, blk, 0, stream>>>(a, total_splits, p.n_chunks, p.chunk_rows, p.nr);
+  else if (total_splits > 128)
+    merge_kernel<D, 8, 8><<<g8, blk, 0, stream>>>(a, total_splits, p.n_chunks, p.chunk_rows, p.nr);
+  else if (total_splits > 64)
+    merge_kernel<D, 8, 4><<<g8, blk, 0, stream>>>(a, total_splits, p.n_chunks, p.chunk_rows, p.nr);
+  else if (total_splits > 32)
+    merge_kernel<D, 8, 2><<<g8, blk, 0, stream>>>(a, total_splits, p.n_chunks, p.chunk_rows, p.nr);
   else
-    merge_kernel<D, 8><<<dim3(rows, D / 32), dim3(256), 0, stream>>>(a, total_splits, p.n_chunks,
-                                                                    p.chunk_rows, p.nr);
+    merge_kernel<D, 8, 1><<<g8, blk, 0, stream>>>(a, total_splits, p.n_chunks, p.chunk_rows, p.nr);
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const AttnArgs& a, const SplitPlan& p, int total_splits, hipStream_t stream) {
+hipError_t launch_merge(const AttnArgs& args, const SplitPlan& p, int total_splits, hipStream_t stream) {
+  const AttnArgs a = with_divisors(args, p);
   switch (a.head_dim) {
     case 64: return launch_merge<64>(a, p, total_splits, stream);
     case 128: return launch_merge<128>(a, p, total_splits, stream);
@@ -1340,7 +1364,8 @@ hipError_t launch_attention(const AttnArgs& a, const SplitPlan& p, int dtype, hi
   return launch_merge(a, p, a.part_stride, stream);
 }
 
-hipError_t launch_partials(const AttnArgs& a, const SplitPlan& p, int dtype, hipStream_t stream) {
+hipError_t launch_partials(const AttnArgs& args, const SplitPlan& p, int dtype, hipStream_t stream) {
+  const AttnArgs a = with_divisors(args, p);
   const bool bf16 = dtype == WMTP_BF16;
   if (p.coop) {
     switch (a.head_dim) {

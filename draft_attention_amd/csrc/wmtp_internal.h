@@ -56,6 +56,25 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
 
 enum AttnMode { kModeWindowed = 0, kModeFull = 1, kModeVerify = 2 };
 
+// Division by a value fixed for a whole call (head counts, group size, candidates, row chunks) as
+// one multiply-high, an add and a shift, exact for dividends below 2^31 (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", PLDI 1994, the round-up
+// multiplier): with s = ceil(log2 d) and mul = floor(2^32 (2^s - d) / d) + 1,
+// x / d = (umulhi(x, mul) + x) >> s. A run-time division otherwise costs a dependent sequence of
+// about twenty instructions, several of which stand between a kernel's start and its first load.
+struct FastDiv {
+  uint32_t d, mul, shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d < 1 ? 1 : d;
+  f.shift = 0;
+  while ((1ull << f.shift) < f.d) ++f.shift;
+  f.mul = (uint32_t)(((1ull << 32) * ((1ull << f.shift) - f.d)) / f.d + 1);
+  return f;
+}
+
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -83,6 +102,9 @@ struct AttnArgs {
   const void* new_k;
   const void* new_v;
   int32_t* pos;
+  // divisors of the index arithmetic, filled by the launchers from the sizes above and the plan:
+  // n_q_heads, n_kv_heads, G = n_q_heads / n_kv_heads, m, row chunks, rows per chunk
+  FastDiv div_hq, div_kv, div_g, div_m, div_chunks, div_crows;
 };
 
 // split kernel (or cooperative kernel) writing partials, then the log-sum-exp merge over

@@ -67,6 +67,8 @@ def copy_calibration():
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_decode_step_L1M.txt")
+TRACE_SUMMARY = os.path.join(ROOT, "profiles", "kernel_trace_decode_step_L1M.txt")
+GATE_FRAC = 0.75  # each gated read must reach this share of the HBM peak
 
 
 def attn_source_hash() -> str:
@@ -79,18 +81,100 @@ def attn_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kind: str):
-    """HBM bytes per launch (profiler FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading)
-    from the committed summary, or None when the attention source changed since it was taken."""
+def summary_fields(path: str):
+    """The `key: value` lines of a committed profile summary, or None when the attention source
+    changed since its numbers were taken (its recorded source hash differs)."""
     try:
-        with open(TRAFFIC_SUMMARY) as fh:
+        with open(path) as fh:
             fields = dict(l.split(": ", 1) for l in fh.read().splitlines() if ": " in l)
     except OSError:
         return None
     if fields.get("attn_source_sha256", "").strip() != attn_source_hash():
         return None
-    v = fields.get(f"traffic_bytes_per_launch.{kind}")
+    return {k.strip(): v.strip() for k, v in fields.items()}
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch (profiler FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading)
+    from the committed summary, or None when the attention source changed since it was taken."""
+    fields = summary_fields(TRAFFIC_SUMMARY)
+    v = None if fields is None else fields.get(f"traffic_bytes_per_launch.{kind}")
     return None if v is None else int(float(v))
+
+
+def traced_kernel_us(kind: str):
+    """Average kernel-only duration (us) of one kernel of a call from the committed rocprofv3
+    kernel trace (kind e.g. windowed.split, windowed.merge), or None when the source changed."""
+    fields = summary_fields(TRACE_SUMMARY)
+    v = None if fields is None else fields.get(f"kernel_us.{kind}")
+    return None if v is None else float(v)
+
+
+def host_cpu():
+    """Model name of the host CPU and the cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def capture(fn):
+    """A HIP graph of the work fn enqueues, captured on a side stream. (torch.cuda.graph() would
+    first call torch.cuda.empty_cache(); releasing cached device memory to the driver leaves the
+    long attention kernels about 5% slower for the rest of the process, so the benchmark never
+    does it.)"""
+    import torch
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g.capture_begin()
+        try:
+            fn()
+        finally:
+            g.capture_end()
+    torch.cuda.current_stream().wait_stream(side)
+    return g
+
+
+def graph_us(fn, calls: int = 100, reps: int = 3) -> float:
+    """Per-call time of `calls` invocations of fn captured in one HIP graph and replayed back to
+    back (no host launch gaps, no event per call); the best of `reps` replays."""
+    import torch
+
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+
+    def body():
+        for _ in range(calls):
+            fn()
+    g = capture(body)
+    g.replay()
+    torch.cuda.synchronize()
+    best = float("inf")
+    stream = torch.cuda.current_stream()
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = min(best, 1000.0 * e0.elapsed_time(e1) / calls)
+    del g
+    return best
 
 
 def fill_sequence(dst, seed, tensor_id, b, p0, p1, dtype, device, chunk=1 << 17):
@@ -209,16 +293,13 @@ def main():
     else:
         # one HIP graph per phase (captured once, replayed): the kernels of a phase run back to
         # back on the GPU, as inside a serving engine's captured decode loop. Every replay
-        # appends (the same token bytes) at the next positions, so caches keep growing. On
-        # ROCm 7 the long attention kernels run about 4% slower when launched from a graph than
-        # when launched directly, which is why this is not the default.
+        # appends (the same token bytes) at the next positions, so caches keep growing. Graphs
+        # are captured without releasing cached memory (see capture()), so replays run as fast
+        # as direct launches.
         graphs = {}
         for name, f in phases.items():
             for append in (True, False):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    f(0, append)
-                graphs[(name, append)] = g
+                graphs[(name, append)] = capture(lambda f=f, append=append: f(0, append))
         run = {name: (lambda nm: (lambda s, append=True: graphs[(nm, append)].replay()))(name)
                for name in phases}
         launch = "hip-graph (one captured graph per phase, replayed)"
@@ -267,9 +348,37 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             attn_only[name].append(e0.elapsed_time(e1))
+    # the same single calls graph-replayed back to back (no host launch gaps or per-call events),
+    # the windowed call also cold (each call behind a 512 MiB cache flush, the flush's own time
+    # subtracted), and the launch floors beside the windowed read
+    log("graph-replayed single calls and launch floors")
+    t_mid = args.warmup * k
+    calls_of = {
+        "win": lambda: W.wmtp_draft_attn_windowed(ring, draft_q[t_mid], Hq, scale3, out3, lse3, ws_win),
+        "full": lambda: W.wmtp_draft_attn_full(full, draft_q[t_mid], Hq, scale3, cap, out3, lse3, ws_full),
+        "ver": lambda: W.wmtp_verify_attn(tgt, ver_q[args.warmup], m, Hq4, scale4, cap4, out4, lse4, ws_ver),
+    }
+    call_graph_us = {"win": graph_us(calls_of["win"], 200), "full": graph_us(calls_of["full"], 20),
+                     "ver": graph_us(calls_of["ver"], 20)}
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush = lambda: W.wmtp_llc_flush(flush_buf)
+    win_cold_graph = graph_us(lambda: (flush(), calls_of["win"]()), 50) - graph_us(flush, 50)
+    tiny = torch.empty(256, dtype=torch.uint8, device=dev)
+    ring_copy = torch.empty(2 * ring.k.numel() * ring.k.element_size(), dtype=torch.uint8, device=dev)
+    floors = {
+        "one_launch_us": round(graph_us(lambda: W.wmtp_llc_flush(tiny), 200), 3),
+        "two_launches_us": round(graph_us(lambda: (W.wmtp_llc_flush(tiny), W.wmtp_llc_flush(tiny)), 200), 3),
+        "ring_bytes_read_one_launch_us": round(graph_us(lambda: W.wmtp_probe_read(ring_copy, probe_out), 200), 3),
+        "note": "graph-replayed, back to back: an (almost) empty kernel of the library "
+                "(wmtp_llc_flush of 256 bytes), two of them, and the read probe streaming as "
+                "many bytes as the ring's K and V once; the windowed call is two dependent "
+                "launches (split-K partials, then the merge)",
+    }
+    del flush_buf, ring_copy
     masw_res = None if args.no_composite else masw_step(
         W, synth, D3, full, ring, Hq, scale3, stream, ev, log)
-    other = None if args.no_sweep else other_workloads(W, synth, configs, stream, ev, log)
+    other = None if args.no_sweep else other_workloads(W, synth, configs, stream, ev, log,
+                                                         cpu=not args.no_cpu_baseline)
     comp = None if args.no_composite else composite(
         W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log)
     read_ceiling = read_probe(W, probe_buf, probe_out, stream, ev)
@@ -350,6 +459,23 @@ def main():
         "other_workloads": other,
         "masw": masw_res,
         "sweep": sweep_res,
+        "gates": {
+            "windowed": gate("windowed draft attention (split-K kernel + LSE merge), 4100 ring "
+                             "slots, 32q/2kv, d256, bf16", b_win, mean_us["win_attn"],
+                             call_graph_us["win"], win_cold_graph, "windowed", floors),
+            "full": gate("full-context draft attention (split-K kernel + LSE merge), L=1048576, "
+                         "32q/2kv, d256, bf16", b_full, mean_us["full_attn"], call_graph_us["full"],
+                         None, "full"),
+            "verify": gate("verification attention m=4 (cooperative MFMA kernel + LSE merge), "
+                           "L=1048576, 32q/2kv, d128, bf16", b_ver, mean_us["ver_attn"],
+                           call_graph_us["ver"], None, "verify"),
+            "note": "call_us: event-timed calls back to back behind a backlog read (as *_attn in "
+                    "draft_step_us); call_us_graph: graph-replayed; kernel_us_trace / merge_us_trace: "
+                    "kernel-only means from the committed rocprofv3 kernel trace "
+                    "(profiles/kernel_trace_decode_step_L1M.txt), traffic: FETCH_SIZE + WRITE_SIZE of "
+                    "both kernels (profiles/hbm_traffic_decode_step_L1M.txt), both null when the "
+                    "attention source changed since they were taken; pass_*: frac >= 0.75",
+        },
         "roofline": {
             "kernel": "full-context draft attention call (split-K attention + LSE merge, "
                       "back to back), L=1048576, 32q/2kv, d256, bf16",
@@ -367,23 +493,58 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(full, tgt, ring, draft_q, ver_q, k, m, S, Wn,
-                                              scale3, scale4, step_bytes, log)
+                                              scale3, scale4, step_bytes, log, other,
+                                              call_graph_us)
     print(json.dumps(result), flush=True)
+
+
+def gate(desc, nbytes, call_us, call_us_graph, cold_us_graph, kind, floors=None):
+    """Per-kernel gate entry: the call's and the kernel's share of the HBM peak, with the traced
+    kernel-only times and the measured traffic of both kernels (split-K or cooperative + merge)."""
+    frac = lambda us: None if us is None else round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+    k_us = traced_kernel_us(f"{kind}.main")
+    m_us = traced_kernel_us(f"{kind}.merge")
+    t_main, t_merge = measured_traffic(kind), measured_traffic(f"{kind}_merge")
+    traffic = None if t_main is None or t_merge is None else t_main + t_merge
+    entry = {
+        "kernel": desc,
+        "algorithmic_bytes": int(nbytes),
+        "call_us": round(call_us, 3), "call_frac": frac(call_us),
+        "call_us_graph": round(call_us_graph, 3), "call_frac_graph": frac(call_us_graph),
+        "kernel_us_trace": k_us, "kernel_frac_trace": frac(k_us),
+        "merge_us_trace": m_us,
+        "traffic_bytes": traffic,
+        "traffic_over_algorithmic": None if traffic is None else round(traffic / nbytes, 4),
+        "target_frac": GATE_FRAC,
+        "pass_call": frac(call_us) >= GATE_FRAC,
+        "pass_kernel": None if k_us is None else frac(k_us) >= GATE_FRAC,
+    }
+    if cold_us_graph is not None:
+        entry["call_us_cold_graph"] = round(cold_us_graph, 3)
+        entry["call_frac_cold_graph"] = frac(cold_us_graph)
+    if floors is not None:
+        entry["floors"] = floors
+        entry["floor_frac_read_one_launch"] = frac(floors["ring_bytes_read_one_launch_us"])
+    return entry
 
 
 CPU_REPS = 3  # oracle repetitions per timed part (about 10 s of CPU work on 16 threads)
 COMPOSITE_VOCAB = 131072  # synthetic target vocabulary for the greedy acceptance step
-COMPOSITE_MARGIN = 512  # cache room for the tokens the composite keeps (a + 1 per iteration)
+COMPOSITE_MARGIN = 4096  # cache room for the tokens the composite keeps (a + 1 per iteration)
 
 
 def composite(W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log, iters: int = 8,
               depths=(1, 2, 3, 4, 5)):
-    """One speculative decode iteration at L = 1M, attention side only, for draft depths k:
-    k draft steps (append + attend; windowed ring with k slack slots, or the contiguous cache),
-    the target's append + verification of the k+1 candidates, greedy acceptance on synthetic
-    logits, and the rollback of the rejected tokens in the draft cache and the target cache.
-    Also the no-speculation decode step (the target appends one token and attends everything).
-    Per-token cost for an acceptance of a drafts = iteration cost / (a + 1) tokens."""
+    """One speculative decode iteration at L = 1M, attention side only, for draft depths k and
+    every acceptance a = 0..k: k draft steps (append + attend; windowed ring with k slack slots,
+    or the contiguous cache), the target's append + verification of the k+1 candidates, greedy
+    acceptance on synthetic logits, and the rollback of the k - a rejected tokens in the draft
+    cache and the target cache. The draft tokens are built from the logits' argmax so that
+    exactly a of them are accepted (checked on the device after the timed iterations), so each
+    (k, a) iteration does its own accept and rollback work. Per-token cost = iteration cost /
+    (a + 1) tokens. Also the no-speculation decode step (the target appends one token and attends
+    everything)."""
+    import numpy as np
     import torch
 
     dev = full.k.device
@@ -414,23 +575,33 @@ def composite(W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log, iters: in
     ws_full = W.workspace(1, Hq, Hkv, d, 1, cap, dev)
     V = COMPOSITE_VOCAB
     g = torch.Generator(device="cpu").manual_seed(D3.seed)
-    logits = torch.randn((1, kmax + 1, V), generator=g).to(dt).to(dev)
-    drafts = torch.zeros((1, kmax), dtype=torch.int32, device=dev)
+    logits_host = torch.randn((1, kmax + 1, V), generator=g).to(dt)
+    logits = logits_host.to(dev)
+    # the target's greedy choice per row (first maximum), from the same bf16 values
+    pick = np.argmax(logits_host.float().numpy()[0], axis=1)
     choice = torch.empty((1, kmax + 1), dtype=torch.int32, device=dev)
     n_acc, nxt, n_drop = (torch.empty((1,), dtype=torch.int32, device=dev) for _ in range(3))
-    res = {"vocab": V, "depths": list(depths), "windowed_iter_us": [], "full_iter_us": [],
-           "reduction": [], "per_token_us": {}}
+    res = {"vocab": V, "depths": list(depths), "windowed_iter_us": {}, "full_iter_us": {},
+           "reduction": {}, "per_token_us": {}, "accepted_checked": True}
 
-    def iteration(form, k):
+    def drafts_for(k, a):
+        """k draft tokens of which exactly the first a equal the target's choices."""
+        dr = [int(pick[i]) for i in range(a)]
+        if a < k:
+            dr.append(int((pick[a] + 1) % V))
+        dr += [int(pick[i]) for i in range(len(dr), k)]
+        return torch.tensor([dr], dtype=torch.int32, device=dev)
+
+    def iteration(form, k, a):
         ws_acc = W.accept_workspace(1, k, V, dev)
         ws_ver = W.workspace(1, Hq4, Hkv4, d4, k + 1, cap4, dev)
         lg = logits[:, :k + 1].contiguous()
-        dr = drafts[:, :k].contiguous()
+        dr = drafts_for(k, a)
         ch = choice[:, :k + 1].contiguous()
         qk = q4[:, :k + 1].contiguous()  # made once here, not a copy inside the timed iteration
+        cache = ring if form == "windowed" else full
 
         def run():
-            cache = ring if form == "windowed" else full
             for i in range(k):
                 if form == "windowed":
                     W.wmtp_draft_step_windowed(ring, tok_k[i:i + 1][None], tok_v[i:i + 1][None],
@@ -458,16 +629,23 @@ def composite(W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log, iters: in
         return us[len(us) // 2]
 
     for k in depths:
-        tw = timed(iteration("windowed", k))
-        tf = timed(iteration("full", k))
-        res["windowed_iter_us"].append(round(tw, 1))
-        res["full_iter_us"].append(round(tf, 1))
-        res["reduction"].append(round(1.0 - tw / tf, 4))
+        tw, tf = [], []
+        for a in range(k + 1):
+            tw.append(timed(iteration("windowed", k, a)))
+            ok = int(n_acc.item()) == a
+            tf.append(timed(iteration("full", k, a)))
+            ok = ok and int(n_acc.item()) == a
+            res["accepted_checked"] = res["accepted_checked"] and ok
+        res["windowed_iter_us"][str(k)] = [round(x, 1) for x in tw]
+        res["full_iter_us"][str(k)] = [round(x, 1) for x in tf]
+        res["reduction"][str(k)] = [round(1.0 - w / f, 4) for w, f in zip(tw, tf)]
         res["per_token_us"][str(k)] = {
-            "windowed": [round(tw / (a + 1), 1) for a in range(k + 1)],
-            "full": [round(tf / (a + 1), 1) for a in range(k + 1)]}
-        log(f"composite k={k}: windowed {tw:.1f} us, full {tf:.1f} us per iteration")
-    # caches are back where they started (every iteration rolls back what it did not keep)
+            "windowed": [round(tw[a] / (a + 1), 1) for a in range(k + 1)],
+            "full": [round(tf[a] / (a + 1), 1) for a in range(k + 1)]}
+        log(f"composite k={k}: windowed {[round(x) for x in tw]} us, full {[round(x) for x in tf]} us "
+            f"per iteration for a = 0..{k}")
+    # every iteration rolls back what it did not accept, so the caches only grow by the accepted
+    # tokens (draft cache) and accepted + 1 (target)
     assert int(full.seq_len.item()) >= n0 and int(tgt.seq_len.item()) >= n4
     one_k = cand_k[:1][None]
     one_v = cand_v[:1][None]
@@ -480,21 +658,39 @@ def composite(W, synth, D3, V4, full, tgt, cap, cap4, stream, ev, log, iters: in
                            ws1)
         W.wmtp_ring_rollback(tgt, one)  # keep the cache length fixed across repetitions
     res["no_speculation_step_us"] = round(timed(nospec), 1)
-    res["note"] = ("attention-side cost of one decode iteration (eager launches); tokens per "
-                   "iteration = accepted drafts a + 1; per_token_us[k][a] = iteration / (a+1); "
-                   "no_speculation_step_us includes a rollback of the token it appends")
+    res["note"] = ("attention-side cost of one decode iteration (eager launches) for draft depth k "
+                   "and exactly a accepted drafts (lists indexed by a = 0..k; the drafts are built "
+                   "from the synthetic logits' argmax and the device's acceptance count is checked: "
+                   "accepted_checked); tokens per iteration = a + 1; per_token_us = iteration / "
+                   "(a + 1); no_speculation_step_us includes a rollback of the token it appends")
     return res
 
 
-def other_workloads(W, synth, configs, stream, ev, log, calls: int = 100):
-    """Draft steps of the mid-context workload (L = 131072, 32q/4kv, d128, S4, W2048; windowed
-    and full, cold and warm) and of the batched ring workload (8 ragged sequences, 16q/2kv, d128,
-    S4, W2048; windowed), each a fused step (append + attend), median of `calls` calls after 20
-    warm-up calls. The appended tokens are discarded again (rollback), so every call sees the same
-    lengths."""
+def oracle_time(fn, reps: int = 3) -> float:
+    """Mean wall time (us) of `reps` calls of an oracle function on the host."""
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    return (time.perf_counter() - t0) / reps * 1e6
+
+
+def other_workloads(W, synth, configs, stream, ev, log, calls: int = 100, cpu: bool = False):
+    """Draft steps of the tiny workload (L = 4096, fp32, 8q/2kv, d64, S4, W256), the mid-context
+    workload (L = 131072, 32q/4kv, d128, S4, W2048) and the batched ring workload (8 ragged
+    sequences, 16q/2kv, d128, S4, W2048):
+      * attention-only calls, graph-replayed back to back (*_attn_us_graph);
+      * for the mid-context and batched workloads also the fused step (append + attend, then a
+        rollback of the token, so every call sees the same lengths): cold (each call after a
+        cache flush, events around it; p50/p10/p90 of `calls`) and warm (graph-replayed);
+      * with cpu=True, the float64 oracle on the same bytes (oracle_us, host cores).
+    """
+    import numpy as np
     import torch
 
-    dt = torch.bfloat16
+    oracle = None
+    if cpu:
+        import oracle as oracle_mod
+        oracle = oracle_mod
     dev = torch.device("cuda:0")
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     res = {}
@@ -502,24 +698,13 @@ def other_workloads(W, synth, configs, stream, ev, log, calls: int = 100):
     def time_calls(fn, cold):
         """cold: each call after a 512 MiB flush, events around the call (the flush keeps the GPU
         busy while the host queues the call, so the events bracket GPU work); p50/p10/p90.
-        warm: `calls` calls captured in one HIP graph and replayed once (back to back on the GPU,
-        no host launch gaps); mean."""
+        warm: `calls` calls captured in one HIP graph and replayed (back to back, no host launch
+        gaps); mean."""
+        if not cold:
+            return {"mean": round(graph_us(fn, calls, reps=1), 2)}
         for _ in range(20):
             fn()
         torch.cuda.synchronize()
-        if not cold:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for _ in range(calls):
-                    fn()
-            g.replay()
-            torch.cuda.synchronize()
-            e0, e1 = ev(), ev()
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return {"mean": round(1000.0 * e0.elapsed_time(e1) / calls, 2)}
         pairs = []
         for _ in range(calls):
             W.wmtp_llc_flush(flush_buf)
@@ -533,8 +718,42 @@ def other_workloads(W, synth, configs, stream, ev, log, calls: int = 100):
         return {"p50": round(us[len(us) // 2], 2), "p10": round(us[len(us) // 10], 2),
                 "p90": round(us[(9 * len(us)) // 10], 2)}
 
+    # ---- tiny draft step (fp32)
+    T = configs.TINY
+    L, Hq, Hkv, d, S, Wn = T.context, T.n_q_heads, T.n_kv_heads, T.head_dim, T.sink, T.window
+    f32 = torch.float32
+    n = L + 1
+    full = W.KVCache.contiguous(1, Hkv, d, n, f32, dev)
+    full.k[0] = synth.sequence_rows(T.seed, synth.K_ID, 0, 0, n, Hkv, d, f32, dev)
+    full.v[0] = synth.sequence_rows(T.seed, synth.V_ID, 0, 0, n, Hkv, d, f32, dev)
+    full.seq_len.fill_(n)
+    ring = W.KVCache.ring(1, Hkv, d, S, Wn, f32, dev)
+    W.wmtp_ring_append(ring, full.k[0].permute(1, 0, 2).contiguous()[None],
+                       full.v[0].permute(1, 0, 2).contiguous()[None], n)
+    q = synth.queries(T.seed, 0, 1, 1, Hq, d, f32, dev)
+    out = torch.empty((1, 1, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((1, 1, Hq), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    ws_f = W.workspace(1, Hq, Hkv, d, 1, n, dev)
+    ws_w = W.workspace(1, Hq, Hkv, d, 1, ring.capacity, dev)
+    res["tiny"] = {
+        "workload": T.name,
+        "full_attn_us_graph": round(graph_us(lambda: W.wmtp_draft_attn_full(
+            full, q, Hq, scale, n, out, lse, ws_f), calls), 3),
+        "windowed_attn_us_graph": round(graph_us(lambda: W.wmtp_draft_attn_windowed(
+            ring, q, Hq, scale, out, lse, ws_w), calls), 3)}
+    if cpu:
+        kv = oracle.contiguous_kv(synth.host_array(full.k), synth.host_array(full.v), oracle.F32)
+        qh = synth.host_array(q)
+        res["tiny"]["oracle_us"] = {
+            "full_attn": round(oracle_time(lambda: oracle.draft_full(qh, oracle.F32, kv, [n], scale)), 1),
+            "windowed_attn": round(oracle_time(lambda: oracle.draft_windowed(
+                qh, oracle.F32, kv, [n], S, Wn, scale)), 1)}
+    del full, ring
+
     # ---- mid-context draft step
     M = configs.MID
+    dt = torch.bfloat16
     L, Hq, Hkv, d, S, Wn = M.context, M.n_q_heads, M.n_kv_heads, M.head_dim, M.sink, M.window
     cap = L + 16
     full = W.KVCache.contiguous(1, Hkv, d, cap, dt, dev)
@@ -569,13 +788,26 @@ def other_workloads(W, synth, configs, stream, ev, log, calls: int = 100):
 
     res["mid_context"] = {
         "workload": M.name,
+        "full_attn_us_graph": round(graph_us(lambda: W.wmtp_draft_attn_full(
+            full, q, Hq, scale, cap, out, lse, ws_f), 20), 3),
+        "windowed_attn_us_graph": round(graph_us(lambda: W.wmtp_draft_attn_windowed(
+            ring, q, Hq, scale, out, lse, ws_w), calls), 3),
         "full_step_us_cold": time_calls(step_full, True),
         "windowed_step_us_cold": time_calls(step_win, True),
         "full_step_us_warm": time_calls(step_full, False),
         "windowed_step_us_warm": time_calls(step_win, False),
         "note": "step = fused append + attend, then a rollback of the token (kernel ~3 us)"}
-    log(f"mid-context: full {res['mid_context']['full_step_us_cold']['p50']} us, windowed "
-        f"{res['mid_context']['windowed_step_us_cold']['p50']} us (cold p50)")
+    if cpu:
+        kv = oracle.contiguous_kv(synth.host_array(full.k[:, :, :L]),
+                                  synth.host_array(full.v[:, :, :L]), oracle.BF16)
+        qh = synth.host_array(q)
+        res["mid_context"]["oracle_us"] = {
+            "full_attn": round(oracle_time(lambda: oracle.draft_full(qh, oracle.BF16, kv, [L], scale)), 1),
+            "windowed_attn": round(oracle_time(lambda: oracle.draft_windowed(
+                qh, oracle.BF16, kv, [L], S, Wn, scale)), 1)}
+        del kv
+    log(f"mid-context: full {res['mid_context']['full_attn_us_graph']} us, windowed "
+        f"{res['mid_context']['windowed_attn_us_graph']} us (attention, graph-replayed)")
     del full, ws_f
 
     # ---- batched ring draft step
@@ -583,14 +815,21 @@ def other_workloads(W, synth, configs, stream, ev, log, calls: int = 100):
     B, Hq, Hkv, d, S, Wn = Bc.batch, Bc.n_q_heads, Bc.n_kv_heads, Bc.head_dim, Bc.sink, Bc.window
     lens = [synth.uniform_int(Bc.seed, synth.LEN_ID, b, Bc.ragged_lo, Bc.context) for b in range(B)]
     ring = W.KVCache.ring(B, Hkv, d, S, Wn, dt, dev, slack=1)
+    held = []  # host copies of what each ring holds: (positions, K rows, V rows)
     for b, n in enumerate(lens):  # the ring state after n appends: sinks and the last W + 1 tokens
         sub = W.KVCache(ring.k[b:b + 1], ring.v[b:b + 1], ring.pos[b:b + 1], ring.seq_len[b:b + 1],
                         1, Hkv, d, ring.capacity, S, Wn, ring.dtype)
+        rows_k, rows_v = [], []
         for p0, p1 in ((0, S), (n - Wn - 1, n)):
             sub.seq_len.fill_(p0)
-            W.wmtp_ring_append(sub, synth.token_rows(Bc.seed, synth.K_ID, b, p0, p1, Hkv, d, dt, dev)[None],
-                               synth.token_rows(Bc.seed, synth.V_ID, b, p0, p1, Hkv, d, dt, dev)[None],
-                               p1 - p0)
+            rk = synth.token_rows(Bc.seed, synth.K_ID, b, p0, p1, Hkv, d, dt, dev)
+            rv = synth.token_rows(Bc.seed, synth.V_ID, b, p0, p1, Hkv, d, dt, dev)
+            W.wmtp_ring_append(sub, rk[None], rv[None], p1 - p0)
+            rows_k.append(rk)
+            rows_v.append(rv)
+        if cpu:
+            held.append((n, torch.cat(rows_k).permute(1, 0, 2).contiguous(),
+                         torch.cat(rows_v).permute(1, 0, 2).contiguous()))
     kn = torch.stack([synth.token_rows(Bc.seed, synth.KNEW_ID, b, 0, 1, Hkv, d, dt, dev)
                       for b in range(B)])
     vn = torch.stack([synth.token_rows(Bc.seed, synth.VNEW_ID, b, 0, 1, Hkv, d, dt, dev)
@@ -600,18 +839,30 @@ def other_workloads(W, synth, configs, stream, ev, log, calls: int = 100):
     lse = torch.empty((B, 1, Hq), dtype=torch.float32, device=dev)
     ones = torch.ones((B,), dtype=torch.int32, device=dev)
     ws_w = W.workspace(B, Hq, Hkv, d, 1, ring.capacity, dev)
+    scale = 1.0 / math.sqrt(d)
 
     def step_batched():
-        W.wmtp_draft_step_windowed(ring, kn, vn, q, Hq, 1.0 / math.sqrt(d), out, lse, ws_w)
+        W.wmtp_draft_step_windowed(ring, kn, vn, q, Hq, scale, out, lse, ws_w)
         W.wmtp_ring_rollback(ring, ones)
 
-    warm = time_calls(step_batched, False)
     nbytes = 2 * B * (S + Wn) * Hkv * d * 2
-    res["batched"] = {"workload": Bc.name, "windowed_step_us_warm": warm,
+    res["batched"] = {"workload": Bc.name,
+                      "windowed_attn_us_graph": round(graph_us(lambda: W.wmtp_draft_attn_windowed(
+                          ring, q, Hq, scale, out, lse, ws_w), calls), 3),
+                      "windowed_step_us_warm": time_calls(step_batched, False),
                       "windowed_step_us_cold": time_calls(step_batched, True),
                       "attended_kv_bytes": nbytes,
                       "note": "step = fused append + attend for all 8 sequences, then a rollback"}
-    log(f"batched: windowed step {warm['mean']} us (warm, graph replay)")
+    if cpu:
+        # the rings' rows with their logical positions: sinks, then the last W + 1 positions
+        hk = np.stack([synth.host_array(k) for _, k, _ in held])
+        hv = np.stack([synth.host_array(v) for _, _, v in held])
+        segs = [[(0, 0, S), (n - Wn - 1, S, Wn + 1)] for n, _, _ in held]
+        kv = oracle.LogicalKV(hk, hv, oracle.BF16, segs)
+        qh = synth.host_array(q)
+        res["batched"]["oracle_us"] = {"windowed_attn": round(oracle_time(
+            lambda: oracle.draft_windowed(qh, oracle.BF16, kv, lens, S, Wn, scale)), 1)}
+    log(f"batched: windowed attention {res['batched']['windowed_attn_us_graph']} us (graph-replayed)")
     return res
 
 
@@ -774,11 +1025,13 @@ def sweep(W, synth, D3, full, cap, Hq, scale, probe_buf, probe_out, stream, ev, 
     return res
 
 
-def cpu_baseline(full, tgt, ring, draft_q, ver_q, k, m, S, Wn, scale3, scale4, step_bytes, log):
+def cpu_baseline(full, tgt, ring, draft_q, ver_q, k, m, S, Wn, scale3, scale4, step_bytes, log,
+                 other=None, gpu_calls=None):
     """The float64 oracle, as it stands, on the host cores: one full-context draft step, one
-    windowed draft step and one verification over the same caches, scaled to a whole step."""
+    windowed draft step and one verification over the same caches, scaled to a whole step; and,
+    per workload, the oracle's time per attention call beside the GPU's (graph-replayed)."""
     import oracle
-    from draft_attention_amd import synth
+    from draft_attention_amd import configs, synth
 
     threads = oracle.max_threads()
     n3 = int(full.seq_len.item())
@@ -804,6 +1057,26 @@ def cpu_baseline(full, tgt, ring, draft_q, ver_q, k, m, S, Wn, scale3, scale4, s
     t_ver = timed(lambda: oracle.verify(q4, oracle.BF16, kv4, [n4], scale4), reps)
     t_step = k * (t_full + t_win) + t_ver
     log(f"cpu baseline: full {t_full:.2f}s windowed {t_win * 1e3:.1f}ms verify {t_ver:.2f}s")
+    per_config = {
+        configs.MILLION.name: {
+            "oracle_us": {"full_attn": round(t_full * 1e6, 1), "windowed_attn": round(t_win * 1e6, 1)},
+            "gpu_us": None if gpu_calls is None else {"full_attn": round(gpu_calls["full"], 3),
+                                                      "windowed_attn": round(gpu_calls["win"], 3)}},
+        configs.VERIFY.name: {
+            "oracle_us": {"verify_attn": round(t_ver * 1e6, 1)},
+            "gpu_us": None if gpu_calls is None else {"verify_attn": round(gpu_calls["ver"], 3)}},
+    }
+    for key in ("tiny", "mid_context", "batched"):
+        w = (other or {}).get(key)
+        if not w or "oracle_us" not in w:
+            continue
+        gpu = {f"{form}_attn": w[f"{form}_attn_us_graph"] for form in ("full", "windowed")
+               if f"{form}_attn_us_graph" in w}
+        per_config[w["workload"]] = {"oracle_us": w["oracle_us"], "gpu_us": gpu}
+    for v in per_config.values():
+        if v["gpu_us"]:
+            v["oracle_over_gpu"] = {c: round(v["oracle_us"][c] / v["gpu_us"][c], 1)
+                                    for c in v["oracle_us"] if c in v["gpu_us"]}
     return {
         "value": round(step_bytes / t_step / 1e9, 3),
         "unit": "GB/s",
@@ -814,6 +1087,11 @@ def cpu_baseline(full, tgt, ring, draft_q, ver_q, k, m, S, Wn, scale3, scale4, s
                    f"(mean); whole step = 5 x (full + windowed) + verify = {t_step:.2f} s"),
         "draft_step_us": {"full_attn": round(t_full * 1e6, 1), "windowed_attn": round(t_win * 1e6, 1)},
         "verify_us": round(t_ver * 1e6, 1),
+        "host": dict(host_cpu(), omp_threads=threads),
+        "per_config": per_config,
+        "per_config_note": "oracle_us: mean of 3 oracle calls per attention call (one draft step "
+                           "or one verification) on the host cores; gpu_us: the same call "
+                           "graph-replayed on the GPU",
     }
 
 

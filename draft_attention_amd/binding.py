@@ -67,6 +67,7 @@ def lib():
         L.wmtp_draft_step_windowed.argtypes = [kvp, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
         L.wmtp_draft_step_full.argtypes = [kvp, vp, vp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
         L.wmtp_verify_step.argtypes = [kvp, vp, vp, vp, i32, i32, f32, i32, vp, vp, vp, sz, vp]
+        L.wmtp_draft_step_windowed_noalloc.argtypes = [kvp, vp, vp, vp, i32, f32, vp, vp, vp]
         L.wmtp_draft_attn_masw.argtypes = [kvp, kvp, vp, i32, f32, i32, vp, vp, vp, sz, vp]
         L.wmtp_masw_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
         L.wmtp_masw_workspace_bytes.restype = sz
@@ -78,7 +79,7 @@ def lib():
         for name in ("wmtp_ring_append", "wmtp_draft_attn_windowed", "wmtp_draft_attn_full",
                      "wmtp_verify_attn", "wmtp_ring_rollback", "wmtp_greedy_accept",
                      "wmtp_draft_attn_masw", "wmtp_draft_step_windowed", "wmtp_draft_step_full",
-                     "wmtp_verify_step",
+                     "wmtp_verify_step", "wmtp_draft_step_windowed_noalloc",
                      "wmtp_probe_read", "wmtp_llc_flush"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -324,6 +325,19 @@ def wmtp_draft_step_windowed(ring, k_new, v_new, q, n_q_heads: int, sm_scale: fl
                                         int(n_q_heads), float(sm_scale), _ptr(out), _ptr(lse),
                                         _ptr(ws), int(nbytes), _stream(stream))
     return _done(st, "wmtp_draft_step_windowed", check)
+
+
+def wmtp_draft_step_windowed_noalloc(ring, k_new, v_new, q, n_q_heads: int, sm_scale: float, out,
+                                     lse, stream=None, check=True) -> int:
+    """wmtp_draft_step_windowed with the partials in the library's static device scratch (no
+    workspace; allocates nothing)."""
+    d = _desc(ring)
+    _check_append(d, k_new, v_new, 1)
+    _check_attn(d, q, 1, n_q_heads, out, lse)
+    st = lib().wmtp_draft_step_windowed_noalloc(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                                int(n_q_heads), float(sm_scale), _ptr(out),
+                                                _ptr(lse), _stream(stream))
+    return _done(st, "wmtp_draft_step_windowed_noalloc", check)
 
 
 def wmtp_draft_step_full(cache, k_new, v_new, q, n_q_heads: int, sm_scale: float,

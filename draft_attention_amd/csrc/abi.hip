@@ -1,9 +1,12 @@
 // abi.hip -- the extern "C" entry points of libwmtp.so (declared and documented in wmtp.h):
-// host-side validation, split planning and launches. No allocation, no synchronisation, no global
-// state.
+// host-side validation, split planning and launches. No allocation and no synchronisation. The
+// only state is the per-device address of the allocation-free entry point's static scratch
+// array (below), looked up once per device.
 
 #include <math.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "wmtp_internal.h"
 
@@ -148,9 +151,53 @@ size_t masw_bytes(const SplitPlan& pr, const SplitPlan& ps) {
   return plan_bytes(both);
 }
 
+// ---- scratch of the allocation-free windowed draft step (wmtp_draft_step_windowed_noalloc)
+// Device memory of the split-K partials, part of the library's code object: every GPU the library
+// runs on holds its own copy from the first use of the library on it until the process ends.
+// Host code must not pass `scratch` itself to a kernel (in host code the name is a host-side
+// stand-in, not a device address): its device address is looked up once per device with
+// hipGetSymbolAddress and kept in scratch_addr.
+constexpr size_t kScratchBytes = WMTP_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices];
+
+// The current device's scratch address (looked up on the first call on that device), or NULL
+// when the HIP runtime cannot report it.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_addr[dev] = p;
+  }
+  return scratch_addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+int wmtp_draft_step_windowed_noalloc(const wmtp_kv* ring, const void* k_new, const void* v_new,
+                                     const void* q, int32_t n_q_heads, float sm_scale, float* out,
+                                     float* lse, void* stream) {
+  int st = check_kv(ring);
+  if (st != WMTP_OK) return st;
+  if (ring->window < 1 || !k_new || !v_new) return WMTP_ERR_INVALID_ARG;
+  // the partials this step needs must fit the static scratch (checked before any lookup)
+  const size_t need = wmtp_attn_workspace_bytes(ring->batch, n_q_heads, ring->n_kv_heads,
+                                                ring->head_dim, 1, ring->capacity);
+  if (need == 0) return WMTP_ERR_INVALID_ARG;
+  if (need > kScratchBytes) return WMTP_ERR_WORKSPACE;
+  void* ws = device_scratch();
+  if (!ws) return WMTP_ERR_HIP;
+  // the partials are written in full before the merge reads them: nothing must start at zero
+  return attention_call(ring, q, 1, n_q_heads, sm_scale, ring->capacity, wmtp::kModeWindowed, out,
+                        lse, ws, kScratchBytes, stream, k_new, v_new);
+}
 
 int wmtp_ring_append(const wmtp_kv* cache, const void* k_new, const void* v_new, int32_t n_new,
                      void* stream) {

@@ -238,6 +238,24 @@ int wmtp_verify_step(const wmtp_kv* cache, const void* k_new, const void* v_new,
                      int32_t m, int32_t n_q_heads, float sm_scale, int32_t max_seq_len, float* out,
                      float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): exactly wmtp_draft_step_windowed(ring, k_new, v_new,
+ * q, n_q_heads, sm_scale, out, lse, ws, ws_bytes, stream), with the same kernels, results, ring
+ * bytes, tags and seq_len, but with no workspace argument: the split-K partials go to a static
+ * device array of WMTP_NOALLOC_SCRATCH_BYTES that the library's code object holds on every GPU it
+ * runs on until the process ends. The call allocates and frees nothing. Its device address is
+ * looked up (hipGetSymbolAddress) on the first call on each device, so the current device must be
+ * the one `stream` belongs to. Every call on a GPU shares that GPU's array: calls that may overlap
+ * on one GPU (other streams, other host threads) race and must be serialised by the caller. The
+ * partials are written in full before they are read, so the array needs no clearing.
+ * Errors: as for wmtp_draft_step_windowed; WMTP_ERR_WORKSPACE when the step needs more than
+ * WMTP_NOALLOC_SCRATCH_BYTES (wmtp_attn_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
+ * 1, capacity) is the need); WMTP_ERR_HIP when the array's address cannot be obtained. */
+#define WMTP_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int wmtp_draft_step_windowed_noalloc(const wmtp_kv* ring, const void* k_new, const void* v_new,
+                                     const void* q, int32_t n_q_heads, float sm_scale, float* out,
+                                     float* lse, void* stream);
+
 /* Workspace bytes an attention call with these sizes needs (split-K partial results). Pass
  * m = 1 for draft steps and max_seq_len = capacity for the windowed call. Depends only on its
  * arguments (not on the device). Returns 0 for arguments no attention call accepts. */

@@ -34,7 +34,8 @@ def test_exports_every_declared_function(lib):
                           "wmtp_probe_read", "wmtp_llc_flush", "wmtp_ring_rollback",
                           "wmtp_greedy_accept", "wmtp_accept_workspace_bytes",
                           "wmtp_draft_attn_masw", "wmtp_masw_workspace_bytes",
-                          "wmtp_draft_step_windowed", "wmtp_draft_step_full", "wmtp_verify_step"}
+                          "wmtp_draft_step_windowed", "wmtp_draft_step_full", "wmtp_verify_step",
+                          "wmtp_draft_step_windowed_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -325,3 +326,21 @@ def test_cache_descriptor_checks_the_cache_tensors():
     c.seq_len = _DeviceTensor(1, 4)  # fewer lengths than sequences: refused at the rebuild
     with pytest.raises(ValueError, match="seq_len"):
         c.desc()
+
+
+def test_noalloc_step_arguments_rejected_before_launch(lib):
+    """The allocation-free windowed step validates like the workspace step, and refuses a step
+    whose partials exceed its static scratch, before looking up the scratch or launching."""
+    L = W.lib()
+    call = lambda desc, k_new=FAKE, v_new=FAKE, q=FAKE, hq=8: L.wmtp_draft_step_windowed_noalloc(
+        desc, k_new, v_new, q, hq, 0.1, FAKE, None, None)
+    assert call(None) == W.WMTP_ERR_INVALID_ARG
+    assert call(ctypes.byref(_kv(window=0, sink=20))) == W.WMTP_ERR_INVALID_ARG  # not a ring
+    assert call(ctypes.byref(_kv()), k_new=None) == W.WMTP_ERR_INVALID_ARG
+    assert call(ctypes.byref(_kv(head_dim=96))) == W.WMTP_ERR_UNSUPPORTED
+    assert call(ctypes.byref(_kv()), hq=7) == W.WMTP_ERR_INVALID_ARG
+    # 2048 (sequence, KV head) pairs need at least one 16 KB partial each: 32 MB of partials
+    big = _kv(batch=1024, n_kv_heads=2, head_dim=256, capacity=260, sink=4, window=256)
+    need = L.wmtp_attn_workspace_bytes(1024, 32, 2, 256, 1, 260)
+    assert need > 16 << 20
+    assert call(ctypes.byref(big), hq=32) == W.WMTP_ERR_WORKSPACE

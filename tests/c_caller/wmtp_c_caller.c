@@ -6,8 +6,12 @@
  * It builds a compact ring buffer (the Windowed-MTP abstract's last sentence: S sink slots plus W
  * window slots) and a contiguous cache from the same N tokens, appending all of them with
  * wmtp_ring_append. It then runs one windowed draft read over the ring, which attends the sinks and
- * the last W tokens, and one full-context read over the cache, which attends all N tokens. It also
- * checks two refused calls. Inputs and outputs are written as raw little-endian files into OUTDIR.
+ * the last W tokens, and one full-context read over the cache, which attends all N tokens. A third
+ * cache, contiguous, takes the same N tokens and then the target's verification of MV candidates
+ * (wmtp_verify_step: append MV candidate tokens and attend them causally, MV * GQ = 32 query rows
+ * per KV head) and a second verification of the last MV3 positions (wmtp_verify_attn, MV3 * GQ =
+ * 12 rows). It also checks three refused calls. Inputs and outputs are written as raw
+ * little-endian files into OUTDIR.
  *
  * Inputs: xorshift64* (Vigna, "An experimental exploration of Marsaglia's xorshift generators,
  * scrambled", ACM TOMS 2016) draws, uniform in [-1, 1), truncated to bf16.
@@ -24,7 +28,8 @@
 
 #include "wmtp.h"
 
-enum { HKV = 2, GQ = 4, HQ = HKV * GQ, D = 128, S = 4, W = 64, N = 300 };
+enum { HKV = 2, GQ = 4, HQ = HKV * GQ, D = 128, S = 4, W = 64, N = 300, MV = 8, MV3 = 3 };
+enum { NV = N + MV, NV_CAP = NV + 5 };  /* verification cache: length after the step, capacity */
 
 static uint64_t rng_state = 0x9E3779B97F4A7C15ull;
 
@@ -103,13 +108,30 @@ int main(int argc, char** argv) {
   for (size_t i = 0; i < tok_elems; ++i) kn[i] = next_bf16();
   for (size_t i = 0; i < tok_elems; ++i) vn[i] = next_bf16();
   for (size_t i = 0; i < (size_t)HQ * D; ++i) q[i] = next_bf16();
+  const size_t cand_elems = (size_t)MV * HKV * D;  /* candidates, [1][MV][HKV][D] */
+  const size_t qv_elems = (size_t)MV * HQ * D, qv3_elems = (size_t)MV3 * HQ * D;
+  uint16_t* kc = malloc(cand_elems * 2);
+  uint16_t* vcn = malloc(cand_elems * 2);
+  uint16_t* qv = malloc(qv_elems * 2);
+  uint16_t* qv3 = malloc(qv3_elems * 2);
+  if (!kc || !vcn || !qv || !qv3) return 1;
+  for (size_t i = 0; i < cand_elems; ++i) kc[i] = next_bf16();
+  for (size_t i = 0; i < cand_elems; ++i) vcn[i] = next_bf16();
+  for (size_t i = 0; i < qv_elems; ++i) qv[i] = next_bf16();
+  for (size_t i = 0; i < qv3_elems; ++i) qv3[i] = next_bf16();
 
   void *d_kn, *d_vn, *d_q, *rk, *rv, *ck, *cv, *ws_w, *ws_f;
   int32_t *rpos, *rlen, *clen;
   float *out_w, *lse_w, *out_f, *lse_f;
   const size_t wsb_w = wmtp_attn_workspace_bytes(1, HQ, HKV, D, 1, (int32_t)ring_slots);
   const size_t wsb_f = wmtp_attn_workspace_bytes(1, HQ, HKV, D, 1, N);
-  if (wsb_w == 0 || wsb_f == 0) {
+  const size_t wsb_v = wmtp_attn_workspace_bytes(1, HQ, HKV, D, MV, NV);
+  const size_t wsb_v3 = wmtp_attn_workspace_bytes(1, HQ, HKV, D, MV3, NV);
+  const size_t vc_elems = (size_t)HKV * NV_CAP * D;
+  void *d_kc, *d_vcn, *d_qv, *d_qv3, *vk, *vv, *ws_v, *ws_v3;
+  int32_t* vlen;
+  float *out_v, *lse_v, *out_v3, *lse_v3;
+  if (wsb_w == 0 || wsb_f == 0 || wsb_v == 0 || wsb_v3 == 0) {
     fprintf(stderr, "no workspace size for these shapes\n");
     return 1;
   }
@@ -129,6 +151,24 @@ int main(int argc, char** argv) {
   HIP_OK(hipMalloc((void**)&lse_f, (size_t)HQ * 4));
   HIP_OK(hipMalloc(&ws_w, wsb_w));  /* hipMalloc returns 256-byte aligned memory */
   HIP_OK(hipMalloc(&ws_f, wsb_f));
+  HIP_OK(hipMalloc(&d_kc, cand_elems * 2));
+  HIP_OK(hipMalloc(&d_vcn, cand_elems * 2));
+  HIP_OK(hipMalloc(&d_qv, qv_elems * 2));
+  HIP_OK(hipMalloc(&d_qv3, qv3_elems * 2));
+  HIP_OK(hipMalloc(&vk, vc_elems * 2));
+  HIP_OK(hipMalloc(&vv, vc_elems * 2));
+  HIP_OK(hipMalloc((void**)&vlen, 4));
+  HIP_OK(hipMalloc((void**)&out_v, qv_elems * 4));  /* float32 [1][MV][HQ][D] */
+  HIP_OK(hipMalloc((void**)&lse_v, (size_t)MV * HQ * 4));
+  HIP_OK(hipMalloc((void**)&out_v3, qv3_elems * 4));
+  HIP_OK(hipMalloc((void**)&lse_v3, (size_t)MV3 * HQ * 4));
+  HIP_OK(hipMalloc(&ws_v, wsb_v));
+  HIP_OK(hipMalloc(&ws_v3, wsb_v3));
+  HIP_OK(hipMemcpy(d_kc, kc, cand_elems * 2, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_vcn, vcn, cand_elems * 2, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_qv, qv, qv_elems * 2, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(d_qv3, qv3, qv3_elems * 2, hipMemcpyHostToDevice));
+  HIP_OK(hipMemset(vlen, 0, 4));
   HIP_OK(hipMemcpy(d_kn, kn, tok_elems * 2, hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(d_vn, vn, tok_elems * 2, hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(d_q, q, (size_t)HQ * D * 2, hipMemcpyHostToDevice));
@@ -147,6 +187,15 @@ int main(int argc, char** argv) {
   WMTP_OK_(wmtp_draft_attn_windowed(&ring, d_q, HQ, scale, out_w, lse_w, ws_w, wsb_w, NULL));
   WMTP_OK_(wmtp_draft_attn_full(&cache, d_q, HQ, scale, N, out_f, lse_f, ws_f, wsb_f, NULL));
 
+  /* verification: the prefix, then the MV candidates appended and verified in one call, then the
+   * last MV3 positions verified again by the attention-only call */
+  wmtp_kv vcache = {vk, vv, NULL, vlen, 1, HKV, D, NV_CAP, NV_CAP, 0, WMTP_BF16};
+  WMTP_OK_(wmtp_ring_append(&vcache, d_kn, d_vn, N, NULL));
+  WMTP_OK_(wmtp_verify_step(&vcache, d_kc, d_vcn, d_qv, MV, HQ, scale, NV, out_v, lse_v, ws_v,
+                            wsb_v, NULL));
+  WMTP_OK_(wmtp_verify_attn(&vcache, d_qv3, MV3, HQ, scale, NV, out_v3, lse_v3, ws_v3, wsb_v3,
+                            NULL));
+
   /* refused before anything is launched: half the workspace, and a windowed read of a cache that
    * is not a ring */
   if (wmtp_draft_attn_windowed(&ring, d_q, HQ, scale, out_w, lse_w, ws_w, wsb_w / 2, NULL) !=
@@ -157,6 +206,11 @@ int main(int argc, char** argv) {
   if (wmtp_draft_attn_windowed(&cache, d_q, HQ, scale, out_w, lse_w, ws_w, wsb_w, NULL) !=
       WMTP_ERR_INVALID_ARG) {
     fprintf(stderr, "a contiguous cache was accepted by the windowed read\n");
+    return 1;
+  }
+  if (wmtp_verify_attn(&vcache, d_qv, 17, HQ, scale, NV, out_v, lse_v, ws_v, wsb_v, NULL) !=
+      WMTP_ERR_INVALID_ARG) {
+    fprintf(stderr, "a verification of 17 candidates was accepted\n");
     return 1;
   }
   if (!wmtp_status_string(WMTP_ERR_WORKSPACE)) return 1;
@@ -171,7 +225,16 @@ int main(int argc, char** argv) {
       fetch_and_dump(dir, "ring_k.bin", rk, ring_elems * 2) ||
       fetch_and_dump(dir, "ring_v.bin", rv, ring_elems * 2) ||
       fetch_and_dump(dir, "ring_pos.bin", rpos, ring_slots * 4) ||
-      fetch_and_dump(dir, "ring_len.bin", rlen, 4) || fetch_and_dump(dir, "cache_len.bin", clen, 4))
+      fetch_and_dump(dir, "ring_len.bin", rlen, 4) || fetch_and_dump(dir, "cache_len.bin", clen, 4) ||
+      dump(dir, "k_cand.bin", kc, cand_elems * 2) || dump(dir, "v_cand.bin", vcn, cand_elems * 2) ||
+      dump(dir, "q_verify.bin", qv, qv_elems * 2) || dump(dir, "q_verify3.bin", qv3, qv3_elems * 2) ||
+      fetch_and_dump(dir, "out_verify_step.bin", out_v, qv_elems * 4) ||
+      fetch_and_dump(dir, "lse_verify_step.bin", lse_v, (size_t)MV * HQ * 4) ||
+      fetch_and_dump(dir, "out_verify.bin", out_v3, qv3_elems * 4) ||
+      fetch_and_dump(dir, "lse_verify.bin", lse_v3, (size_t)MV3 * HQ * 4) ||
+      fetch_and_dump(dir, "verify_k.bin", vk, vc_elems * 2) ||
+      fetch_and_dump(dir, "verify_v.bin", vv, vc_elems * 2) ||
+      fetch_and_dump(dir, "verify_len.bin", vlen, 4))
     return 1;
   printf("wmtp_c_caller: ok\n");
   return 0;

@@ -14,7 +14,8 @@ from dataclasses import dataclass
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libwmtp.so")
+# WMTP_LIB names another build of the same sources to load (e.g. one with host-side sanitizers)
+LIB_PATH = os.environ.get("WMTP_LIB") or os.path.join(_HERE, "libwmtp.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "wmtp.h")
 HEADERS = [HEADER, os.path.join(os.path.dirname(_HERE), "include", "wmtp_probe.h")]
 

@@ -27,13 +27,18 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source to an object (all at once) and link libwmtp.so. Returns its path."""
-    objdir = os.path.join(PKG, "_build")
+def build(verbose: bool = False, out: str = LIB, host_flags=()) -> str:
+    """Compile every source to an object (all at once) and link libwmtp.so. Returns its path.
+
+    ``out``: where the library goes (objects beside it in ``_build`` for another path);
+    ``host_flags``: extra flags for the host pass only (each passed as -Xarch_host FLAG, at compile
+    and link time), e.g. sanitizers for a CPU-side check of the argument validation."""
+    objdir = os.path.join(PKG if out == LIB else os.path.dirname(os.path.abspath(out)), "_build")
     os.makedirs(objdir, exist_ok=True)
+    host = [x for f in host_flags for x in ("-Xarch_host", f)]
     common = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-              "-I", INCLUDE, "-I", CSRC]
+              "-I", INCLUDE, "-I", CSRC] + host
     procs = []
     objs = []
     for src in SOURCES:
@@ -45,8 +50,8 @@ def build(verbose: bool = False) -> str:
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     failed = []
     for src, p in procs:
-        out, _ = p.communicate()
-        text = out.decode(errors="replace")
+        log, _ = p.communicate()
+        text = log.decode(errors="replace")
         noise = "is not a recognized feature for this target"
         shown = "\n".join(l for l in text.splitlines() if noise not in l)
         if shown.strip() and (verbose or p.returncode != 0):
@@ -55,13 +60,13 @@ def build(verbose: bool = False) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    tmp = out + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + host + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

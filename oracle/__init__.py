@@ -56,6 +56,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "wmtp_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# another build of wmtp_oracle.c to load instead (the sanitizer run of the CPU tests sets it)
+_LIB_OVERRIDE = os.environ.get("WMTP_ORACLE_LIB")
 
 F32, BF16, F64 = 0, 1, 2
 
@@ -65,15 +67,16 @@ Range = Tuple[int, int]  # half-open [start, stop)
 # --------------------------------------------------------------------------------------------
 # build / load of the C core
 # --------------------------------------------------------------------------------------------
-def build(verbose: bool = False) -> str:
-    """Compile ``wmtp_oracle.c`` into ``liboracle.so`` with gcc (plain -O2, OpenMP, IEEE)."""
+def build(verbose: bool = False, out: str = _LIB_PATH, flags: Sequence[str] = ()) -> str:
+    """Compile ``wmtp_oracle.c`` into ``liboracle.so`` with gcc (plain -O2, OpenMP, IEEE).
+    ``out`` and ``flags`` (extra gcc flags, e.g. sanitizers) serve other builds of the source."""
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-           _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+           *flags, _SRC, "-o", out + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
-    return _LIB_PATH
+    os.replace(out + ".tmp", out)
+    return out
 
 
 _RUNS = 4  # position runs per problem (ORACLE_RUNS in wmtp_oracle.c)
@@ -91,9 +94,12 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB_PATH):
+                build()
+            lib = ctypes.CDLL(_LIB_PATH)
         lib.wmtp_oracle_attention.restype = ctypes.c_int
         lib.wmtp_oracle_attention.argtypes = [
             ctypes.c_int64, ctypes.POINTER(_Problem), ctypes.c_int32, ctypes.c_int32,

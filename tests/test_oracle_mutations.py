@@ -82,6 +82,7 @@ def _copy_oracle(dst):
 
 def _run_pins(pkg):
     env = dict(os.environ, OMP_NUM_THREADS="2")
+    env.pop("WMTP_ORACLE_LIB", None)  # the copy loads the library it builds from its own source
     return subprocess.run([sys.executable, "-c", RUNNER, pkg, PINS], cwd=ROOT, env=env,
                           capture_output=True, text=True, timeout=600)
 

@@ -401,19 +401,39 @@ def main():
                      "ver": steady_graph_us(calls_of["ver"], 40)}
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     flush = lambda: W.wmtp_llc_flush(flush_buf)
-    win_cold_graph = graph_us(lambda: (flush(), calls_of["win"]()), 50) - graph_us(flush, 50)
+    flush_us = graph_us(flush, 50)
+    win_cold_graph = graph_us(lambda: (flush(), calls_of["win"]()), 50) - flush_us
     tiny = torch.empty(256, dtype=torch.uint8, device=dev)
     ring_copy = torch.empty(2 * ring.k.numel() * ring.k.element_size(), dtype=torch.uint8, device=dev)
+    # the windowed call's split launch: one 16-key tile per wavefront, four wavefronts per
+    # workgroup, each workgroup leaving 16 rows x d float32 plus 16 (max, sum) pairs
+    cdiv = lambda a, b: -(-a // b)
+    win_groups = Hkv * cdiv(cdiv(S + Wn, 16), 4)
+    part_bytes = 16 * d * 4 + 16 * 8
+    parts_buf = torch.empty(256 * part_bytes, dtype=torch.uint8, device=dev)
+    handoff_out = torch.empty(W.WMTP_PROBE_HANDOFF_BLOCKS, dtype=torch.int32, device=dev)
+    handoff = lambda g: W.wmtp_probe_handoff(ring_copy, g, parts_buf, part_bytes, handoff_out)
+    read_ring = lambda: W.wmtp_probe_read(ring_copy, probe_out)
     floors = {
         "one_launch_us": round(graph_us(lambda: W.wmtp_llc_flush(tiny), 200), 3),
         "two_launches_us": round(graph_us(lambda: (W.wmtp_llc_flush(tiny), W.wmtp_llc_flush(tiny)), 200), 3),
-        "ring_bytes_read_one_launch_us": round(graph_us(lambda: W.wmtp_probe_read(ring_copy, probe_out), 200), 3),
+        "ring_bytes_read_one_launch_us": round(graph_us(read_ring, 200), 3),
+        "ring_bytes_read_one_launch_cold_us": round(graph_us(lambda: (flush(), read_ring()), 50) - flush_us, 3),
+        "handoff_skeleton_us": {str(g): round(graph_us(lambda g=g: handoff(g), 200), 3)
+                                for g in (win_groups, 256)},
+        "handoff_skeleton_cold_us": {str(g): round(graph_us(lambda g=g: (flush(), handoff(g)), 50) - flush_us, 3)
+                                     for g in (win_groups, 256)},
+        "handoff_part_bytes": part_bytes,
         "note": "graph-replayed, back to back: an (almost) empty kernel of the library "
-                "(wmtp_llc_flush of 256 bytes), two of them, and the read probe streaming as "
-                "many bytes as the ring's K and V once; the windowed call is two dependent "
+                "(wmtp_llc_flush of 256 bytes), two of them, the read probe streaming as many "
+                "bytes as the ring's K and V once, and the hand-off skeleton (wmtp_probe_handoff: "
+                "the ring's bytes read by g workgroups that each write one partial of "
+                "handoff_part_bytes, then 256 workgroups reading the partials back; no arithmetic) "
+                "at the windowed call's own split count and at 256; *_cold: each behind a 512 MiB "
+                "cache flush, the flush's own time subtracted. The windowed call is two dependent "
                 "launches (split-K partials, then the merge)",
     }
-    del flush_buf, ring_copy
+    del flush_buf, ring_copy, parts_buf
     masw_res = None if args.no_composite else masw_step(
         W, synth, D3, full, ring, Hq, scale3, stream, ev, log)
     other = None if args.no_sweep else other_workloads(W, synth, configs, stream, ev, log,

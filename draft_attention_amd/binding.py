@@ -77,11 +77,12 @@ def lib():
         L.wmtp_accept_workspace_bytes.restype = sz
         L.wmtp_probe_read.argtypes = [vp, sz, vp, vp]
         L.wmtp_llc_flush.argtypes = [vp, sz, ctypes.c_uint8, vp]
+        L.wmtp_probe_handoff.argtypes = [vp, sz, i32, vp, sz, vp, vp]
         for name in ("wmtp_ring_append", "wmtp_draft_attn_windowed", "wmtp_draft_attn_full",
                      "wmtp_verify_attn", "wmtp_ring_rollback", "wmtp_greedy_accept",
                      "wmtp_draft_attn_masw", "wmtp_draft_step_windowed", "wmtp_draft_step_full",
                      "wmtp_verify_step", "wmtp_draft_step_windowed_noalloc",
-                     "wmtp_probe_read", "wmtp_llc_flush"):
+                     "wmtp_probe_read", "wmtp_probe_handoff", "wmtp_llc_flush"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -306,6 +307,25 @@ def wmtp_probe_read(buf, out, nbytes: Optional[int] = None, stream=None, check=T
         raise ValueError("wmtp: nbytes exceeds the buffer")
     st = lib().wmtp_probe_read(_ptr(buf), int(n), _ptr(out), _stream(stream))
     return _done(st, "wmtp_probe_read", check)
+
+
+WMTP_PROBE_HANDOFF_BLOCKS = 256  # include/wmtp_probe.h
+
+
+def wmtp_probe_handoff(buf, n_groups: int, parts, part_bytes: int, out, nbytes: Optional[int] = None,
+                       stream=None, check=True) -> int:
+    """Two launches without arithmetic: n_groups workgroups read `nbytes` (default: all) of `buf`,
+    each writing `part_bytes` of partials into `parts`; then WMTP_PROBE_HANDOFF_BLOCKS workgroups
+    read the partials back, out getting one uint32 XOR each."""
+    _numel_ok(out, WMTP_PROBE_HANDOFF_BLOCKS, 4, "out")
+    n = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    if not isinstance(buf, int) and n > buf.numel() * buf.element_size():
+        raise ValueError("wmtp: nbytes exceeds the buffer")
+    if not isinstance(parts, int) and n_groups * part_bytes > parts.numel() * parts.element_size():
+        raise ValueError("wmtp: parts holds fewer than n_groups * part_bytes bytes")
+    st = lib().wmtp_probe_handoff(_ptr(buf), int(n), int(n_groups), _ptr(parts), int(part_bytes),
+                                  _ptr(out), _stream(stream))
+    return _done(st, "wmtp_probe_handoff", check)
 
 
 def wmtp_llc_flush(buf, value: int = 0, stream=None, check=True) -> int:

@@ -31,7 +31,8 @@ def test_exports_every_declared_function(lib):
     names = W.header_functions()
     assert set(names) == {"wmtp_ring_append", "wmtp_draft_attn_windowed", "wmtp_draft_attn_full",
                           "wmtp_verify_attn", "wmtp_attn_workspace_bytes", "wmtp_status_string",
-                          "wmtp_probe_read", "wmtp_llc_flush", "wmtp_ring_rollback",
+                          "wmtp_probe_read", "wmtp_probe_handoff", "wmtp_llc_flush",
+                          "wmtp_ring_rollback",
                           "wmtp_greedy_accept", "wmtp_accept_workspace_bytes",
                           "wmtp_draft_attn_masw", "wmtp_masw_workspace_bytes",
                           "wmtp_draft_step_windowed", "wmtp_draft_step_full", "wmtp_verify_step",
@@ -149,6 +150,18 @@ def test_probe_arguments_rejected_before_launch(lib):
     assert lib.wmtp_llc_flush(None, 1024, 0, None) == W.WMTP_ERR_INVALID_ARG
     assert lib.wmtp_llc_flush(FAKE, 24, 0, None) == W.WMTP_ERR_INVALID_ARG
     assert lib.wmtp_llc_flush(FAKE + 4, 1024, 0, None) == W.WMTP_ERR_INVALID_ARG
+    h = lib.wmtp_probe_handoff
+    assert h(None, 1024, 4, FAKE, 256, out, None) == W.WMTP_ERR_INVALID_ARG
+    assert h(FAKE, 1000, 4, FAKE, 256, out, None) == W.WMTP_ERR_INVALID_ARG
+    assert h(FAKE, 1024, 0, FAKE, 256, out, None) == W.WMTP_ERR_INVALID_ARG
+    assert h(FAKE, 1024, 65536, FAKE, 256, out, None) == W.WMTP_ERR_INVALID_ARG
+    assert h(FAKE, 1024, 2, FAKE, 8, out, None) == W.WMTP_ERR_INVALID_ARG  # product 16, part not
+    assert h(FAKE, 1024, 4, FAKE, 0, out, None) == W.WMTP_ERR_INVALID_ARG
+    assert h(FAKE, 1024, 4, FAKE + 8, 256, out, None) == W.WMTP_ERR_INVALID_ARG
+    assert h(FAKE, 1024, 4, None, 256, out, None) == W.WMTP_ERR_INVALID_ARG
+    assert h(FAKE, 1024, 2, FAKE, 1 << 40, out, None) == W.WMTP_ERR_INVALID_ARG
+    assert h(FAKE, 1024, 4, FAKE, 256, None, None) == W.WMTP_ERR_INVALID_ARG
+    assert h(FAKE, 1024, 4, FAKE, 256, FAKE + 2, None) == W.WMTP_ERR_INVALID_ARG
 
 
 def test_ring_with_slack_is_a_valid_descriptor_and_short_capacity_is_not(lib):

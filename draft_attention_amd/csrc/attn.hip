@@ -29,6 +29,7 @@
 // (row, 32 or 64 dims):
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  o = sum_s o_s 2^(m_s - M) / L,  lse = (M + log2 L) ln 2.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "wmtp_internal.h"
@@ -1260,6 +1261,7 @@ hipError_t launch_coop(const AttnArgs& a, const SplitPlan& p, hipStream_t stream
 #define WMTP_MIN_TILES_PER_WAVE 1
 #endif
 constexpr long long kMinTilesPerWave = WMTP_MIN_TILES_PER_WAVE;
+constexpr int kSplitMaxRows = 48;  // most query rows per KV head on the key-split kernel
 
 // Largest row chunk whose Q operand and O accumulators fit the register file beside the K/V tiles.
 static int rows_cap(int dtype, int head_dim) {
@@ -1274,9 +1276,17 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
   if (m < 1 || m > kMaxM || max_seq_len < 1 || max_seq_len > kMaxCapacity) return false;
   p->G = n_q_heads / n_kv_heads;
   p->rows = p->G * m;
-  // key-split kernel for a single row block (draft steps), cooperative tiles for several (verify);
-  // each with the workgroup count measured best for it on MI355X
-  p->coop = kAllowCoop && p->rows > 16;
+  // Key-split kernel for one row block, and for a verification whose rows fit one of its row
+  // chunks in at most three 16-row blocks; cooperative tiles beyond. Each kernel runs with the
+  // workgroup count measured best for it. Measured on MI355X (verification at 256K-1M keys, steady
+  // state): the key-split kernel wins at 24-48 rows by 8-24% (bf16 head_dim 64/128/256, fp32
+  // 64/128; e.g. bf16 d128 at 32 rows 154 vs 167 us) and loses at 64 rows (four blocks leave no
+  // register room for its prefetch: 208 vs 173 us) and wherever the rows need a second chunk (the
+  // cache is then read twice). Draft steps (one query token) keep the cooperative kernel above 16
+  // rows: the key-split kernel's ring-masked and fused forms take one row block.
+  const bool split_rows =
+      p->rows <= 16 || (m > 1 && p->rows <= std::min(rows_cap(dtype, head_dim), kSplitMaxRows));
+  p->coop = kAllowCoop && !split_rows;
   const int target_blocks = p->coop ? kTargetBlocksCoop : kTargetBlocksSplit;
   // row blocks per cooperative workgroup within the register budget: eight (two per wavefront)
   // for bf16 up to head_dim 128, two for fp32 at head_dim 256, four otherwise

@@ -230,10 +230,12 @@ size_t wmtp_accept_workspace_bytes(int32_t batch, int32_t k, int32_t vocab);
 /* The target's append + verification in one call: wmtp_ring_append(cache, k_new, v_new, m) then
  * wmtp_verify_attn(cache, q, m, ...); k_new/v_new are [batch][m][n_kv_heads][head_dim] and
  * max_seq_len must bound the lengths after the append. When the cooperative kernel runs the
- * verification (more than 16 query rows per KV head) it reads the candidates from k_new/v_new
- * while storing them and the merge advances seq_len (two launches instead of three); otherwise the
- * append runs first. Results, cache bytes and lengths equal the two calls. Errors as for
- * wmtp_verify_attn. */
+ * verification (more query rows per KV head, m * n_q_heads / n_kv_heads, than the key-split
+ * kernel takes: 16 for m = 1, else 48, or 32 for bf16 at head_dim 256 and fp32 at 128, 16 for fp32
+ * at 256) it reads
+ * the candidates from k_new/v_new while storing them and the merge advances seq_len (two launches
+ * instead of three); otherwise the append runs first. Results, cache bytes and lengths equal the
+ * two calls. Errors as for wmtp_verify_attn. */
 int wmtp_verify_step(const wmtp_kv* cache, const void* k_new, const void* v_new, const void* q,
                      int32_t m, int32_t n_q_heads, float sm_scale, int32_t max_seq_len, float* out,
                      float* lse, void* ws, size_t ws_bytes, void* stream);

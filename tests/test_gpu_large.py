@@ -46,7 +46,9 @@ def test_offsets_past_four_gib():
     kv_last = oracle_kv(cache.k[1:2, h:h + 1, :lens[1]], cache.v[1:2, h:h + 1, :lens[1]], "bf16")
     kv_first = oracle_kv(cache.k[0:1, :, :lens[0]], cache.v[0:1, :, :lens[0]], "bf16")
 
-    for m in (1, 2, 4):  # draft step (key-split), verify with 16 rows (key-split) and 32 (cooperative)
+    # draft step (key-split), verify with 16 and 32 rows (key-split: one and two row blocks) and
+    # 48 (cooperative: more than the key-split kernel's 32 rows at head_dim 256)
+    for m in (1, 2, 4, 6):
         q = synth.queries(SEED, m, B, m, Hq, d, dt, DEV)
         say(f"large cache: m={m} on the GPU")
         if m == 1:

@@ -168,19 +168,24 @@ def test_full_bound_below_length_reads_nothing_beyond():
 # ------------------------------------------------------------------------------------------
 # verification: m candidates, causal among themselves
 # ------------------------------------------------------------------------------------------
+# rows per KV head = m * Hq / Hkv; the key-split kernel takes up to 48 (32 for bf16 at head_dim
+# 256 and fp32 at 128, 16 for fp32 at 256), the cooperative kernel the rest
 VERIFY_CASES = [
-    ("bf16", 128, 32, 2, 4, [5000, 64]),
-    ("bf16", 128, 16, 2, 1, [300]),
-    ("bf16", 64, 8, 2, 6, [777, 6]),
-    ("bf16", 256, 16, 2, 2, [1500]),
-    ("bf16", 256, 32, 2, 3, [900]),   # 48 rows: two row chunks
-    ("bf16", 256, 32, 2, 6, [901]),   # 96 rows: three row chunks
-    ("f32", 64, 8, 2, 4, [4097, 2]),
-    ("f32", 128, 8, 1, 3, [999]),
-    ("bf16", 128, 8, 4, 16, [2000]),
-    ("bf16", 128, 32, 2, 6, [3000, 77]),  # 96 rows: one chunk, two row blocks per wavefront
-    ("bf16", 128, 16, 1, 8, [2500]),      # 128 rows
-    ("bf16", 64, 32, 2, 5, [1234]),       # 80 rows at head_dim 64
+    ("bf16", 128, 32, 2, 4, [5000, 64]),  # 64 rows: cooperative
+    ("bf16", 128, 16, 2, 1, [300]),       # 8 rows: key-split
+    ("bf16", 64, 8, 2, 6, [777, 6]),      # 24 rows: key-split, two row blocks
+    ("bf16", 256, 16, 2, 2, [1500]),      # 16 rows: key-split
+    ("bf16", 256, 32, 2, 3, [900]),       # 48 rows: cooperative (past 32 at head_dim 256)
+    ("bf16", 256, 32, 2, 6, [901]),       # 96 rows: cooperative, two row chunks
+    ("f32", 64, 8, 2, 4, [4097, 2]),      # 16 rows: key-split
+    ("f32", 128, 8, 1, 3, [999]),         # 24 rows: key-split, two row blocks
+    ("bf16", 128, 8, 4, 16, [2000]),      # 32 rows: key-split, two row blocks
+    ("bf16", 128, 16, 2, 6, [1300, 33]),  # 48 rows: key-split, three row blocks
+    ("f32", 64, 8, 2, 12, [700]),         # 48 rows: key-split, three row blocks, fp32
+    ("f32", 128, 16, 2, 6, [650]),        # 48 rows: cooperative (past 32 for fp32 at 128)
+    ("bf16", 128, 32, 2, 6, [3000, 77]),  # 96 rows: cooperative, two row blocks per wavefront
+    ("bf16", 128, 16, 1, 8, [2500]),      # 128 rows: cooperative
+    ("bf16", 64, 32, 2, 5, [1234]),       # 80 rows at head_dim 64: cooperative
 ]
 
 
@@ -278,7 +283,8 @@ def test_null_lse_gives_the_same_outputs():
     append_each(ring, K, V, [0] * B, [3000, 700])
     cache = W.KVCache.contiguous(B, Hkv, d, 3008, tdtype(dt))
     append_each(cache, K, V, [0] * B, [3000, 700])
-    for Hq, m in ((16, 1), (16, 4)):  # 8 rows (key-split) and 32 rows (cooperative) per KV head
+    # 8 and 32 rows (key-split: one and two row blocks) and 64 rows (cooperative) per KV head
+    for Hq, m in ((16, 1), (16, 4), (16, 8)):
         q = synth.queries(48, 0, B, m, Hq, d, tdtype(dt), DEV)
         calls = [("verify", lambda o, l: W.wmtp_verify_attn(
             cache, q, m, Hq, 0.1, 3000, o, l, W.workspace(B, Hq, Hkv, d, m, 3000)))]
@@ -328,8 +334,8 @@ def test_bytes_past_the_length_do_not_reach_results(dt, d):
     append_each(ring, K, V, [0] * B, lens)
     slack = W.KVCache.ring(B, Hkv, d, S, Wn, tdtype(dt), slack=3)  # the masked-ring kernels
     append_each(slack, K, V, [0] * B, lens)
-    kn = torch.stack([K[b, :, lens[b]:lens[b] + 4].permute(1, 0, 2) for b in range(B)]).contiguous()
-    vn = torch.stack([V[b, :, lens[b]:lens[b] + 4].permute(1, 0, 2) for b in range(B)]).contiguous()
+    kn = torch.stack([K[b, :, lens[b]:lens[b] + 6].permute(1, 0, 2) for b in range(B)]).contiguous()
+    vn = torch.stack([V[b, :, lens[b]:lens[b] + 6].permute(1, 0, 2) for b in range(B)]).contiguous()
     k1, v1 = kn[:, :1].contiguous(), vn[:, :1].contiguous()  # a draft step's token
 
     def attn(c, q, Hq, m, kind):
@@ -353,9 +359,12 @@ def test_bytes_past_the_length_do_not_reach_results(dt, d):
         return o, l
 
     # G = 4 and 16 (key-split kernel), G = 32 or G = 16 with m = 4 (32 and 64 rows: cooperative
-    # kernel where it runs)
+    # kernel where it runs), G = 8 with m = 3, 4, 6 (verification in 24, 32 and 48 rows: the
+    # key-split kernel with two and three row blocks where they fit its row limit)
     cases = [(8, 1, "windowed", ring), (8, 1, "full", cache), (8, 1, "step_windowed", ring),
              (8, 1, "step_full", cache), (8, 4, "verify", cache), (32, 4, "verify", cache),
+             (16, 3, "verify", cache), (16, 4, "verify", cache), (16, 6, "verify", cache),
+             (16, 4, "verify_step", cache),
              (32, 4, "verify_step", cache), (32, 1, "windowed", ring), (32, 1, "full", cache),
              (8, 1, "windowed", slack), (8, 1, "step_windowed", slack), (64, 1, "windowed", ring),
              (64, 1, "windowed", slack)]
@@ -413,7 +422,8 @@ def test_nan_inside_the_attended_set_propagates(dt, d):
     """One K row (sequence 0, KV head 0) and one V element (sequence 1, KV head 1) hold NaN at
     attended positions: exactly the outputs the oracle makes NaN are NaN (the whole query group
     for the K row, one dimension for the V element), on the key-split kernel (windowed ring, full
-    draft) and the cooperative kernel (verification, a 32-head group)."""
+    draft, verification in 8 and 32 rows per KV head) and the cooperative kernel (draft reads of a
+    32-head group, verification in 64 rows)."""
     B, Hkv, S, Wn, n, bound = 2, 2, 4, 64, 700, 1024
     say(f"NaN inside the attended set: {dt} d={d}")
     K, V = logical_kv(85, B, Hkv, d, n, tdtype(dt))
@@ -434,7 +444,7 @@ def test_nan_inside_the_attended_set_propagates(dt, d):
         o, l = run_full(cache, q, Hq, scale, bound)
         ro, rl = oracle.draft_full(qh, ocode(dt), kv, [n] * B, scale)
         _compare_nan(o, l, ro, rl, dt, f"full Hq={Hq}")
-    for Hq, m in ((16, 4), (8, 2)):
+    for Hq, m in ((16, 4), (8, 2), (32, 4)):
         q = synth.queries(87, m, B, m, Hq, d, tdtype(dt), DEV)
         o, l = run_verify(cache, q, Hq, scale, bound)
         ro, rl = oracle.verify(synth.host_array(q), ocode(dt), kv, [n] * B, scale)

@@ -289,7 +289,8 @@ def oracle_kv_for(K, V, dt):
     ("bf16", 256, 32, 2, 3),    # 48 rows at head_dim 256
     ("bf16", 128, 64, 2, 3),    # 96 rows
     ("bf16", 128, 32, 1, 8),    # 256 rows: two row chunks, both read the new rows
-    ("f32", 64, 8, 2, 6),       # 24 rows, fp32
+    ("f32", 64, 8, 2, 6),       # 24 rows, fp32: key-split kernel (two row blocks), append first
+    ("f32", 64, 16, 2, 8),      # 64 rows, fp32: cooperative kernel, fused
     ("bf16", 128, 8, 2, 2),     # 8 rows: split kernel, append first
 ])
 def test_fused_verify_step_equals_append_then_verify(dt, d, Hq, Hkv, m):

@@ -649,6 +649,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
 // (NB = 1 or 2: each wavefront owns D/4 or D/2 dims of its block's rows and recomputes the 16x16
 // score tile, which is cheap on the matrix cores). Each wavefront writes its own part of the
 // workgroup's partial; no cross-wavefront merge is needed.
+#ifndef WMTP_COOP_EIGHT_WAVES
+#define WMTP_COOP_EIGHT_WAVES 1
+#endif
 template <int D, int NB, bool BF16>
 struct Coop {
   static constexpr int kEB = BF16 ? 2 : 4;
@@ -656,11 +659,6 @@ struct Coop {
   static constexpr int kChunks = kRowBytes / 16;             // 16-byte chunks per key row
   static constexpr int kSwz = (kChunks < 16 ? kChunks : 16) - 1;
   static constexpr int kVSwz = (kChunks / 2 < 8 ? kChunks / 2 : 8) - 1;  // 32-byte segments of V
-  static constexpr int kRbw = NB > kWavesPerBlock ? NB / kWavesPerBlock : 1;  // row blocks/wave
-  static constexpr int kSplitD = NB >= kWavesPerBlock ? 1 : kWavesPerBlock / NB;  // waves per block
-  static constexpr int kDw = D / kSplitD;                     // output dims per wavefront
-  static constexpr int kDpl = kDw / 16;                       // V dims per lane (= output blocks)
-  static constexpr int kQRegs = BF16 ? D / 32 : D / 16;       // 16-byte Q/K pieces per lane
   static constexpr int kTileBytes = 16 * kRowBytes;           // K (or V) bytes of one tile
 #ifdef WMTP_COOP_TPS
   static constexpr int kTps = WMTP_COOP_TPS;                   // tiles per LDS stage (per barrier)
@@ -668,7 +666,20 @@ struct Coop {
   static constexpr int kTps = 1;
 #endif
   static constexpr int kStageBytes = kTps * 2 * kTileBytes;   // K and V of the stage's tiles
-  static constexpr int kLoads = kStageBytes / 16 / kThreads;  // 16-byte loads per thread per stage
+  // Wavefronts per workgroup: eight for eight row blocks (one block each) when a stage gives each
+  // of the 512 threads a 16-byte load, else four. Measured on MI355X (verification at L = 1M,
+  // 32q/2kv, d128, bf16): eight blocks on eight wavefronts 230 us, on four (two blocks each)
+  // 236-241 us; with the padding blocks skipped (below) 80 rows take 185 us instead of 238. Four
+  // blocks on eight wavefronts (each half the dims of one block) took 198 us against 174.
+  static constexpr int kWaves =
+      (WMTP_COOP_EIGHT_WAVES && NB == 8 && kStageBytes >= 16 * 512) ? 8 : kWavesPerBlock;
+  static constexpr int kThreadsC = 64 * kWaves;
+  static constexpr int kRbw = NB > kWaves ? NB / kWaves : 1;    // row blocks per wavefront
+  static constexpr int kSplitD = NB >= kWaves ? 1 : kWaves / NB;  // wavefronts per row block
+  static constexpr int kDw = D / kSplitD;                     // output dims per wavefront
+  static constexpr int kDpl = kDw / 16;                       // V dims per lane (= output blocks)
+  static constexpr int kQRegs = BF16 ? D / 32 : D / 16;       // 16-byte Q/K pieces per lane
+  static constexpr int kLoads = kStageBytes / 16 / kThreadsC;  // 16-byte loads per thread per stage
 #ifdef WMTP_COOP_PREFETCH
   static constexpr int kPrefetch = WMTP_COOP_PREFETCH;       // stages in flight
 #else
@@ -677,7 +688,7 @@ struct Coop {
   // beat 3, 4 and 6 (more loads in flight per CU lowered the achieved bandwidth) and 1.
   static constexpr int kPrefetch = kStageBytes >= 8192 ? 2 : 4;
 #endif
-  static_assert(kLoads >= 1 && kStageBytes % (16 * kThreads) == 0, "stage must split evenly");
+  static_assert(kLoads >= 1 && kStageBytes % (16 * kThreadsC) == 0, "stage must split evenly");
   static_assert(kDpl >= (BF16 ? 2 : 1), "each lane needs a pair of bf16 dims");
 };
 
@@ -700,7 +711,7 @@ template <int D, int NB, bool BF16, bool RING, bool FUSED>
 #ifndef WMTP_COOP_WPC
 #define WMTP_COOP_WPC 2
 #endif
-__global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(AttnArgs a, int n_splits,
+__global__ __launch_bounds__((64 * Coop<D, NB, BF16>::kWaves), WMTP_COOP_WPC) void attn_coop_kernel(AttnArgs a, int n_splits,
                                                                  int n_chunks, int chunk_rows) {
   using C = Coop<D, NB, BF16>;
   typedef typename std::conditional<BF16, bf16x8_t, f32x4_t>::type QVec;
@@ -739,7 +750,7 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   QVec qf[C::kRbw][C::kQRegs];
 #pragma unroll
   for (int j = 0; j < C::kRbw; ++j) {
-    const int row = chunk * chunk_rows + (rb0 + kWavesPerBlock * j) * 16 + r16;
+    const int row = chunk * chunk_rows + (rb0 + C::kWaves * j) * 16 + r16;
     row_ok[j] = row < row_end;
     const int row_q = row_ok[j] ? row : row_end - 1;
     const int jq = div_of(row_q, a.div_g);
@@ -777,13 +788,13 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
     return (tl < tiles_lim ? tl : tiles_lim - 1) * kTileKeys;
   };
 
-  // staging: load l of this thread is chunk q = tid + kThreads*l of the stage: tile q / (32*kChunks),
+  // staging: load l of this thread is chunk q = tid + kThreadsC*l of the stage: tile q / (32*kChunks),
   // then K chunks before V chunks
   uint4 stg[C::kPrefetch][C::kLoads];
   auto load_stage = [&](uint4(&dst)[C::kLoads], int stage) {
 #pragma unroll
     for (int l = 0; l < C::kLoads; ++l) {
-      const int q = tid + kThreads * l;
+      const int q = tid + C::kThreadsC * l;
       const int u = q / (32 * C::kChunks);  // tile of the stage
       const int tensor = (q / (16 * C::kChunks)) & 1;
       const int key = (q / C::kChunks) % 16;
@@ -811,7 +822,7 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
     const bool clip = tile_start(stage * C::kTps + C::kTps - 1) + kTileKeys - 1 > clip_last;
 #pragma unroll
     for (int l = 0; l < C::kLoads; ++l) {
-      const int q = tid + kThreads * l;
+      const int q = tid + C::kThreadsC * l;
       const int u = q / (32 * C::kChunks);
       const int tensor = (q / (16 * C::kChunks)) & 1;
       const int key = (q / C::kChunks) % 16;
@@ -838,7 +849,7 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   if constexpr (FUSED) {
     if (split == 0 && chunk == 0) {
       constexpr int kPieces = C::kRowBytes / 16;
-      for (int i = tid; i < 2 * a.m * kPieces; i += kThreads) {
+      for (int i = tid; i < 2 * a.m * kPieces; i += C::kThreadsC) {
         const int tensor = i / (a.m * kPieces);
         const int j = (i / kPieces) % a.m;
         const int c = i % kPieces;
@@ -1003,6 +1014,11 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
     }
   };
 
+  // A wavefront whose one row block lies wholly past the chunk's last row (padding up to the
+  // planned block count, e.g. 80 rows run as 8 blocks) stages its share of the tiles and meets the
+  // barriers but computes nothing.
+  const bool wave_live =
+      C::kRbw > 1 || __builtin_amdgcn_readfirstlane(rb0 * 16) < row_end - chunk * chunk_rows;
   // Rounds of exactly kPrefetch tiles with no early exit: tiles past the workgroup's share are
   // computed fully masked. The straight-line round lets the compiler wait for exactly the oldest
   // staged tile (an early exit inside the round makes it drain every load at the round start).
@@ -1016,7 +1032,7 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
       __syncthreads();  // stage st visible; every wavefront is done with stage st-1's buffer
 #pragma unroll
       for (int u = 0; u < C::kTps; ++u)
-        tile_step(sm_tile[buf] + 2 * u * C::kTileBytes, st * C::kTps + u);
+        if (wave_live) tile_step(sm_tile[buf] + 2 * u * C::kTileBytes, st * C::kTps + u);
     }
   }
 
@@ -1027,7 +1043,7 @@ __global__ __launch_bounds__(kThreads, WMTP_COOP_WPC) void attn_coop_kernel(Attn
   for (int j = 0; j < C::kRbw; ++j) {
     const float l_row = xgroup_sum(l_lane[j]);
     if (!row_ok[j]) continue;
-    const int rloc = (rb0 + kWavesPerBlock * j) * 16 + r16;
+    const int rloc = (rb0 + C::kWaves * j) * 16 + r16;
     float* dst = a.ws_o + (part * kRows + rloc) * D + d0;
     if constexpr (BF16) {
       // lane (r16, grp) holds O^T rows 4*grp + t of block e: dims d0 + 16e + 4*grp + t
@@ -1225,12 +1241,12 @@ hipError_t launch_split(const AttnArgs& a, const SplitPlan& p, hipStream_t strea
 template <int D, bool BF16>
 hipError_t launch_coop(const AttnArgs& a, const SplitPlan& p, hipStream_t stream) {
   dim3 grid(p.n_splits, a.batch * a.n_kv_heads * p.n_chunks);
-  dim3 block(kThreads);
   const bool ring = ring_masked(a);
   const bool fused = a.new_k != nullptr;  // fused verification: contiguous cache, one row chunk
   if (ring && fused) return hipErrorInvalidValue;
 #define WMTP_COOP_LAUNCH(NBV)                                                                          \
   do {                                                                                                 \
+    const dim3 block(64 * Coop<D, NBV, BF16>::kWaves);                                                 \
     if (ring) attn_coop_kernel<D, NBV, BF16, true, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); \
     else if (fused) attn_coop_kernel<D, NBV, BF16, false, true><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); \
     else attn_coop_kernel<D, NBV, BF16, false, false><<<grid, block, 0, stream>>>(a, p.n_splits, p.n_chunks, p.chunk_rows); \

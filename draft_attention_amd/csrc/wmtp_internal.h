@@ -33,6 +33,7 @@ constexpr int kWavesPerBlock = 4;   // wavefronts per workgroup (interleaved til
 //   WMTP_ALLOW_COOP                   0: every row count on the key-split kernel
 //   WMTP_COOP_TPS, WMTP_COOP_PREFETCH tiles per LDS stage, stages in flight (cooperative kernel)
 //   WMTP_COOP_WPC                     workgroups per CU the cooperative kernel is compiled for
+//   WMTP_COOP_EIGHT_WAVES             0: eight row blocks on four wavefronts (two blocks each)
 //   WMTP_MIN_TILES_PER_WAVE           smallest share of a wavefront when the planner splits keys
 // workgroups per call (256 CUs), measured best for each kernel on MI355X at L = 1M
 #ifndef WMTP_TARGET_BLOCKS_SPLIT

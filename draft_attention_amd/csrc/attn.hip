@@ -22,8 +22,10 @@
 // wavefronts combine their states through LDS, each wavefront a quarter of the dims, into one
 // partial (o unnormalised, running max in log2 units, running sum) per query row.
 //
-// Kernel 1b (attn_coop_kernel, more rows: verification): the four wavefronts of a workgroup share
-// each tile through an LDS stage (see the comment above the kernel).
+// Kernel 1 also takes a verification of up to three row blocks (48 rows) when they fit one row
+// chunk. Kernel 1b (attn_coop_kernel, more rows: verification): the wavefronts of a workgroup
+// (four, or eight for eight row blocks) share each tile through an LDS stage (see the comment
+// above the kernel).
 //
 // Kernel 2 (merge_kernel): log-sum-exp merge of the partials of every output row, one workgroup per
 // (row, 32 or 64 dims):
@@ -639,16 +641,17 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a, int n_
 }
 
 // ------------------------------------------------------------------------------------------------
-// Cooperative-tile kernel. The four wavefronts of a workgroup consume the SAME 16-key tile, which
-// the whole workgroup stages through LDS: every thread issues fully coalesced 16-byte loads for its
+// Cooperative-tile kernel. The wavefronts of a workgroup (four, or eight: Coop::kWaves) consume the
+// SAME 16-key tile, which the whole workgroup stages through LDS: every thread issues fully coalesced 16-byte loads for its
 // share of the tile (K and V rows are contiguous in HBM), keeps kPrefetch tiles of them in flight
 // in registers, and writes the oldest one into a double-buffered LDS stage (K chunks XOR-swizzled
 // by key so the operand reads below are bank-conflict free). One barrier per tile.
 // The wavefronts split the work of a tile by query-row block (NB = 4: one block of 16 rows each,
-// the verify shape; NB = 8: two blocks each, sharing one V operand read) or by output dimensions
-// (NB = 1 or 2: each wavefront owns D/4 or D/2 dims of its block's rows and recomputes the 16x16
-// score tile, which is cheap on the matrix cores). Each wavefront writes its own part of the
-// workgroup's partial; no cross-wavefront merge is needed.
+// the verify shape; NB = 8: one block each on eight wavefronts, or two blocks each on four,
+// sharing one V operand read) or by output dimensions (NB = 1 or 2: each wavefront owns D/4 or D/2
+// dims of its block's rows and recomputes the 16x16 score tile, which is cheap on the matrix
+// cores). Each wavefront writes its own part of the workgroup's partial; no cross-wavefront merge
+// is needed.
 #ifndef WMTP_COOP_EIGHT_WAVES
 #define WMTP_COOP_EIGHT_WAVES 1
 #endif
@@ -711,8 +714,8 @@ template <int D, int NB, bool BF16, bool RING, bool FUSED>
 #ifndef WMTP_COOP_WPC
 #define WMTP_COOP_WPC 2
 #endif
-__global__ __launch_bounds__((64 * Coop<D, NB, BF16>::kWaves), WMTP_COOP_WPC) void attn_coop_kernel(AttnArgs a, int n_splits,
-                                                                 int n_chunks, int chunk_rows) {
+__global__ __launch_bounds__((64 * Coop<D, NB, BF16>::kWaves), WMTP_COOP_WPC)
+void attn_coop_kernel(AttnArgs a, int n_splits, int n_chunks, int chunk_rows) {
   using C = Coop<D, NB, BF16>;
   typedef typename std::conditional<BF16, bf16x8_t, f32x4_t>::type QVec;
   __shared__ __attribute__((aligned(16))) char sm_tile[2][C::kStageBytes];
@@ -1304,8 +1307,9 @@ bool make_plan_for(int batch, int n_q_heads, int n_kv_heads, int head_dim, int m
       p->rows <= 16 || (m > 1 && p->rows <= std::min(rows_cap(dtype, head_dim), kSplitMaxRows));
   p->coop = kAllowCoop && !split_rows;
   const int target_blocks = p->coop ? kTargetBlocksCoop : kTargetBlocksSplit;
-  // row blocks per cooperative workgroup within the register budget: eight (two per wavefront)
-  // for bf16 up to head_dim 128, two for fp32 at head_dim 256, four otherwise
+  // row blocks per cooperative workgroup within the register budget: eight (one per wavefront on
+  // eight wavefronts, or two per wavefront on four) for bf16 up to head_dim 128, two for fp32 at
+  // head_dim 256, four otherwise
   const int coop_cap = (dtype == WMTP_BF16 && head_dim <= 128) ? 2 * kWavesPerBlock * 16
                        : (dtype == WMTP_F32 && head_dim == 256) ? 32 : kWavesPerBlock * 16;
   const int cap = p->coop ? coop_cap : rows_cap(dtype, head_dim);

@@ -410,7 +410,7 @@ def main():
     cdiv = lambda a, b: -(-a // b)
     win_groups = Hkv * cdiv(cdiv(S + Wn, 16), 4)
     part_bytes = 16 * d * 4 + 16 * 8
-    parts_buf = torch.empty(256 * part_bytes, dtype=torch.uint8, device=dev)
+    parts_buf = torch.empty(max(win_groups, 256) * part_bytes, dtype=torch.uint8, device=dev)
     handoff_out = torch.empty(W.WMTP_PROBE_HANDOFF_BLOCKS, dtype=torch.int32, device=dev)
     handoff = lambda g: W.wmtp_probe_handoff(ring_copy, g, parts_buf, part_bytes, handoff_out)
     read_ring = lambda: W.wmtp_probe_read(ring_copy, probe_out)
